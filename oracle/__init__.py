@@ -1,0 +1,176 @@
+"""Oracle for the selective state-space scan (fp64, CPU).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or run anything in this
+package.  The product path (``selective_state_space_45_amd``) never calls it
+and fails loudly when its HIP library is missing.  The oracle shares no code,
+header, table or helper with the GPU path.
+
+The arithmetic lives in ``sscan_oracle.c`` (plain C, fp64, libm ``exp``,
+``expm1``, ``log1p``; OpenMP only splits independent (batch, channel) rows).
+This module compiles it with gcc and marshals numpy arrays to it.
+
+What it computes, and the passages it follows (the reference pages):
+
+* Delta = softplus(dt + bias): velog.io Mamba review, section 3.2 "Improving SSMs
+  with Selection" (project, add parameter, softplus; Delta has shape (B, L, D)).
+* Zero-order hold for diagonal A, elementwise: Abar = exp(Delta A),
+  Bbar = (Delta A)^-1 (exp(Delta A) - I) Delta B: velog.io review, section
+  "2 State Space Models", "Discretization"; integral form on the fakeeyes2wo
+  "mamba 学习" page, section "MAMBA".
+* h_k = Abar h_{k-1} + Bbar x_k, y_k = C h_k (+ D x_k), then y * silu(z):
+  velog.io review "Discretization" item 3; page-3 report sections 3 and 4.2.
+* Recurrent step on a carried (B, D, N) state: page-3 report section 6 (ssm_step).
+
+Parity status: every function here is pinned by the ``-m "not gpu"`` tests in
+``tests/test_oracle_pins.py`` (closed forms, a hand-derived worked example,
+library routines, brute force and invariants).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sscan_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle_sscan.so")
+
+
+def compile_source(src_path: str, out_path: str, verbose: bool = False) -> str:
+    """Compile a C oracle source with gcc (no fast-math, no contraction) into a shared library."""
+    tmp = out_path + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math",
+           "-ffp-contract=off", "-o", tmp, src_path, "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out_path)
+    return out_path
+
+
+def build(verbose: bool = False) -> str:
+    """Compile ``sscan_oracle.c`` into ``liboracle_sscan.so``."""
+    return compile_source(_SRC, _LIB_PATH, verbose)
+
+
+def _f64(a, shape=None, name="array"):
+    if a is None:
+        return None
+    arr = np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+    if shape is not None and arr.shape != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {arr.shape}")
+    return arr
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+class Oracle:
+    """ctypes front end of one compiled oracle library."""
+
+    def __init__(self, lib_path: str):
+        lib = ctypes.CDLL(lib_path)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        lib.oracle_sscan_fwd.argtypes = [I64, I64, I64, I64] + [P] * 11 + [ctypes.c_int]
+        lib.oracle_sscan_fwd.restype = ctypes.c_int
+        lib.oracle_sscan_step.argtypes = [I64, I64, I64] + [P] * 10 + [ctypes.c_int]
+        lib.oracle_sscan_step.restype = ctypes.c_int
+        lib.oracle_nthreads_default.argtypes = []
+        lib.oracle_nthreads_default.restype = ctypes.c_int
+        self.lib = lib
+        self.last_threads_used = 0
+
+    def default_threads(self) -> int:
+        return int(self.lib.oracle_nthreads_default())
+
+    def sscan_fwd(self, x, dt, A, B, C, D=None, z=None, dt_bias=None, h0=None,
+                  return_last_state: bool = True, nthreads: int = 0
+                  ) -> Tuple[np.ndarray, Optional[np.ndarray]]:
+        """fp64 forward scan.
+
+        x, dt, z: [batch, seqlen, dim]; A: [dim, dstate]; B, C: [batch, seqlen, dstate];
+        D, dt_bias: [dim]; h0: optional initial state [batch, dim, dstate] (zeros if None).
+        Returns (y [batch, seqlen, dim], last_state [batch, dim, dstate] or None).
+        """
+        x = _f64(x, name="x")
+        if x.ndim != 3:
+            raise ValueError("x must be [batch, seqlen, dim]")
+        Bt, L, Dm = x.shape
+        A = _f64(A, name="A")
+        if A.ndim != 2 or A.shape[0] != Dm:
+            raise ValueError("A must be [dim, dstate]")
+        N = A.shape[1]
+        dt = _f64(dt, (Bt, L, Dm), "dt")
+        B = _f64(B, (Bt, L, N), "B")
+        C = _f64(C, (Bt, L, N), "C")
+        D = _f64(D, (Dm,), "D")
+        z = _f64(z, (Bt, L, Dm), "z")
+        dt_bias = _f64(dt_bias, (Dm,), "dt_bias")
+        h0 = _f64(h0, (Bt, Dm, N), "h0")
+        y = np.empty((Bt, L, Dm), dtype=np.float64)
+        hl = np.empty((Bt, Dm, N), dtype=np.float64) if return_last_state else None
+        used = self.lib.oracle_sscan_fwd(Bt, L, Dm, N, _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                                         _ptr(D), _ptr(z), _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(hl),
+                                         int(nthreads))
+        if used < 0:
+            raise ValueError("oracle_sscan_fwd rejected its arguments")
+        self.last_threads_used = used
+        return y, hl
+
+    def sscan_step(self, state, x, dt, A, B, C, D=None, z=None, dt_bias=None, nthreads: int = 0):
+        """fp64 single-token step.  ``state`` [batch, dim, dstate] (float64, C-contiguous)
+        is updated in place; x, dt, z: [batch, dim]; B, C: [batch, dstate].  Returns y [batch, dim]."""
+        if not (isinstance(state, np.ndarray) and state.dtype == np.float64 and state.flags.c_contiguous):
+            raise TypeError("state must be a C-contiguous float64 numpy array (updated in place)")
+        Bt, Dm, N = state.shape
+        x = _f64(x, (Bt, Dm), "x")
+        dt = _f64(dt, (Bt, Dm), "dt")
+        A = _f64(A, (Dm, N), "A")
+        B = _f64(B, (Bt, N), "B")
+        C = _f64(C, (Bt, N), "C")
+        D = _f64(D, (Dm,), "D")
+        z = _f64(z, (Bt, Dm), "z")
+        dt_bias = _f64(dt_bias, (Dm,), "dt_bias")
+        y = np.empty((Bt, Dm), dtype=np.float64)
+        used = self.lib.oracle_sscan_step(Bt, Dm, N, _ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+                                          _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias), _ptr(y), int(nthreads))
+        if used < 0:
+            raise ValueError("oracle_sscan_step rejected its arguments")
+        self.last_threads_used = used
+        return y
+
+
+_default: Optional[Oracle] = None
+
+
+def _load() -> Oracle:
+    global _default
+    if _default is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        _default = Oracle(_LIB_PATH)
+    return _default
+
+
+def default_threads() -> int:
+    return _load().default_threads()
+
+
+def sscan_fwd(*args, **kwargs):
+    """fp64 forward scan (see ``Oracle.sscan_fwd``)."""
+    return _load().sscan_fwd(*args, **kwargs)
+
+
+def sscan_step(*args, **kwargs):
+    """fp64 single-token step (see ``Oracle.sscan_step``)."""
+    return _load().sscan_step(*args, **kwargs)
+
+
+def last_threads_used() -> int:
+    return _load().last_threads_used
