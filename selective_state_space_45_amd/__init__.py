@@ -1,0 +1,175 @@
+"""Python binding of libselscan: the selective state-space scan on MI355X (gfx950).
+
+Argument marshalling only: every step of the scan runs in the HIP kernels of
+``libselscan.so`` (see ``include/selscan.h`` for the operation and its sources on
+the reference pages).  PyTorch supplies device memory and the current stream.
+There is no fallback: if the library is missing, importing this package raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libselscan.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"libselscan.so not found at {LIB_PATH}; build it with "
+        "`python -m selective_state_space_45_amd.build` (hipcc, gfx950)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+
+_lib.sscan_version.argtypes = []
+_lib.sscan_version.restype = ctypes.c_int
+_lib.sscan_last_error.argtypes = []
+_lib.sscan_last_error.restype = ctypes.c_char_p
+_lib.sscan_fwd_workspace_size.argtypes = [_I64, _I64, _I64, _I64, ctypes.c_int]
+_lib.sscan_fwd_workspace_size.restype = _SZ
+_lib.sscan_fwd.argtypes = [_I64, _I64, _I64, _I64, ctypes.c_int] + [_P] * 11 + [_P, _SZ, _P]
+_lib.sscan_fwd.restype = ctypes.c_int
+_lib.sscan_fwd_segmented.argtypes = [_I64, _I64, _I64, _I64, ctypes.c_int] + [_P] * 11 + [_P, _SZ, _I64, _P]
+_lib.sscan_fwd_segmented.restype = ctypes.c_int
+_lib.sscan_step.argtypes = [_I64, _I64, _I64, ctypes.c_int] + [_P] * 11
+_lib.sscan_step.restype = ctypes.c_int
+
+SSCAN_F32, SSCAN_BF16 = 0, 1
+_DTYPES = {torch.float32: SSCAN_F32, torch.bfloat16: SSCAN_BF16}
+STATUS = {0: "SSCAN_OK", 1: "SSCAN_ERR_INVALID_ARG", 2: "SSCAN_ERR_UNSUPPORTED", 3: "SSCAN_ERR_HIP"}
+
+
+class SelScanError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+def version() -> int:
+    return int(_lib.sscan_version())
+
+
+def last_error() -> str:
+    return _lib.sscan_last_error().decode()
+
+
+def library():
+    """The loaded ctypes library (for callers that marshal pointers themselves)."""
+    return _lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise SelScanError(rc, last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _stream(dev) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def fwd_workspace_size(batch: int, seqlen: int, dim: int, dstate: int, dtype=torch.bfloat16) -> int:
+    return int(_lib.sscan_fwd_workspace_size(batch, seqlen, dim, dstate, _DTYPES[dtype]))
+
+
+def sscan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+              D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+              delta_bias: Optional[torch.Tensor] = None, initial_state: Optional[torch.Tensor] = None,
+              return_last_state: bool = False, out: Optional[torch.Tensor] = None,
+              last_state: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+              num_segments: Optional[int] = None):
+    """Forward selective scan.  x, delta, z: [batch, seqlen, dim]; B, C: [batch, seqlen, dstate]
+    (all float32 or all bfloat16); A: [dim, dstate], D, delta_bias: [dim], initial_state:
+    [batch, dim, dstate] (float32).  Returns y, or (y, last_state)."""
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, seqlen, dim]")
+    batch, seqlen, dim = x.shape
+    if x.dtype not in _DTYPES:
+        raise ValueError("x must be float32 or bfloat16")
+    dt = _DTYPES[x.dtype]
+    dstate = A.shape[1] if A.dim() == 2 else -1
+    _dev(x, "x")
+    _dev(delta, "delta", x.dtype, x.shape)
+    _dev(A, "A", torch.float32, (dim, dstate))
+    _dev(B, "B", x.dtype, (batch, seqlen, dstate))
+    _dev(C, "C", x.dtype, (batch, seqlen, dstate))
+    if D is not None:
+        _dev(D, "D", torch.float32, (dim,))
+    if z is not None:
+        _dev(z, "z", x.dtype, x.shape)
+    if delta_bias is not None:
+        _dev(delta_bias, "delta_bias", torch.float32, (dim,))
+    if initial_state is not None:
+        _dev(initial_state, "initial_state", torch.float32, (batch, dim, dstate))
+    y = out if out is not None else torch.empty_like(x)
+    _dev(y, "out", x.dtype, x.shape)
+    ls = last_state
+    if ls is None and return_last_state:
+        ls = torch.empty((batch, dim, dstate), dtype=torch.float32, device=x.device)
+    if ls is not None:
+        _dev(ls, "last_state", torch.float32, (batch, dim, dstate))
+    if workspace is None:
+        need = fwd_workspace_size(batch, seqlen, dim, dstate, x.dtype)
+        if num_segments is not None and num_segments > 1:
+            need = max(need, 4 * num_segments * batch * dim * (2 * dstate + 1))
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device) if need > 0 else None
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = [batch, seqlen, dim, dstate, dt, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+            _ptr(delta_bias), _ptr(initial_state), _ptr(y), _ptr(ls), _ptr(workspace), wbytes]
+    if num_segments is None:
+        _check(_lib.sscan_fwd(*args, _stream(x.device)))
+    else:
+        _check(_lib.sscan_fwd_segmented(*args, int(num_segments), _stream(x.device)))
+    if return_last_state:
+        return y, ls
+    return y
+
+
+def sscan_step(state: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+               C: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+               delta_bias: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode step.  state: [batch, dim, dstate] float32, updated in place; x, delta, z:
+    [batch, dim]; B, C: [batch, dstate] (float32 or bfloat16); A: [dim, dstate].  Returns y [batch, dim]."""
+    if x.dim() != 2:
+        raise ValueError("x must be [batch, dim]")
+    batch, dim = x.shape
+    if x.dtype not in _DTYPES:
+        raise ValueError("x must be float32 or bfloat16")
+    dstate = A.shape[1] if A.dim() == 2 else -1
+    _dev(state, "state", torch.float32, (batch, dim, dstate))
+    _dev(x, "x")
+    _dev(delta, "delta", x.dtype, x.shape)
+    _dev(A, "A", torch.float32, (dim, dstate))
+    _dev(B, "B", x.dtype, (batch, dstate))
+    _dev(C, "C", x.dtype, (batch, dstate))
+    if D is not None:
+        _dev(D, "D", torch.float32, (dim,))
+    if z is not None:
+        _dev(z, "z", x.dtype, x.shape)
+    if delta_bias is not None:
+        _dev(delta_bias, "delta_bias", torch.float32, (dim,))
+    y = out if out is not None else torch.empty_like(x)
+    _dev(y, "out", x.dtype, x.shape)
+    _check(_lib.sscan_step(batch, dim, dstate, _DTYPES[x.dtype], _ptr(state), _ptr(x), _ptr(delta), _ptr(A),
+                           _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(y), _stream(x.device)))
+    return y

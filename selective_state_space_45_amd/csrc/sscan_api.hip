@@ -1,0 +1,267 @@
+// C entry points of libselscan: argument checks, segmentation choice, launches.
+// The operations are defined in include/selscan.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "selscan.h"
+#include "sscan_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return SSCAN_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(SSCAN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Compute units of the current device (cached per device); 256 if the query fails.
+int device_cus() {
+  static std::mutex mu;
+  static std::vector<int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  std::lock_guard<std::mutex> lk(mu);
+  if (static_cast<int>(cache.size()) <= dev) cache.resize(dev + 1, 0);
+  if (cache[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cache[dev] = cus;
+  }
+  return cache[dev];
+}
+
+struct SegPlan {
+  int nseg;
+  int64_t seg_len;
+};
+
+size_t seg_workspace_bytes(int64_t batch, int64_t dim, int64_t N, int nseg) {
+  if (nseg <= 1) return 0;
+  // carry [nseg][B][D][N], end states [nseg][B][D][N], sums [nseg][B][D]
+  return static_cast<size_t>(nseg) * batch * dim * (2 * N + 1) * sizeof(float);
+}
+
+// Segments wanted for a shape: one unless the (batch, channel-tile) grid alone
+// leaves compute units idle; then enough for about two workgroups per CU, with
+// segments of at least four chunks.
+int auto_segments(int64_t batch, int64_t seqlen, int64_t dim) {
+  const int64_t ndt = (dim + sscan::kTile - 1) / sscan::kTile;
+  const int64_t base = ndt * batch;
+  const int64_t cus = device_cus();
+  if (base <= 0 || base >= cus) return 1;
+  int64_t want = (2 * cus + base - 1) / base;
+  const int64_t maxseg = seqlen / (4 * sscan::kChunk);
+  if (want > maxseg) want = maxseg;
+  if (want > 1024) want = 1024;
+  return want < 1 ? 1 : static_cast<int>(want);
+}
+
+SegPlan plan_segments(int64_t batch, int64_t seqlen, int64_t dim, int64_t N, int64_t requested,
+                      size_t ws_bytes, bool have_ws) {
+  int64_t want = requested > 0 ? requested : auto_segments(batch, seqlen, dim);
+  const int64_t maxseg = (seqlen + sscan::kChunk - 1) / sscan::kChunk;
+  if (want > maxseg) want = maxseg;
+  if (want < 1) want = 1;
+  while (want > 1 && (!have_ws || seg_workspace_bytes(batch, dim, N, static_cast<int>(want)) > ws_bytes)) --want;
+  SegPlan pl{1, seqlen};
+  if (want <= 1) return pl;
+  int64_t len = (seqlen + want - 1) / want;
+  len = (len + sscan::kChunk - 1) / sscan::kChunk * sscan::kChunk;
+  pl.seg_len = len;
+  pl.nseg = static_cast<int>((seqlen + len - 1) / len);
+  return pl;
+}
+
+bool overlaps(const void* a, size_t abytes, const void* b, size_t bbytes) {
+  if (!a || !b || abytes == 0 || bbytes == 0) return false;
+  const char* pa = static_cast<const char*>(a);
+  const char* pb = static_cast<const char*>(b);
+  return pa < pb + bbytes && pb < pa + abytes;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_common(int64_t batch, int64_t dim, int64_t dstate, int dtype) {
+  if (dtype != SSCAN_F32 && dtype != SSCAN_BF16) return fail(SSCAN_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+  if (dstate < 1 || dstate > SSCAN_MAX_DSTATE)
+    return fail(SSCAN_ERR_UNSUPPORTED, "dstate %lld outside [1, %d]", (long long)dstate, SSCAN_MAX_DSTATE);
+  if (batch < 0 || dim < 0) return fail(SSCAN_ERR_INVALID_ARG, "negative size (batch %lld, dim %lld)",
+                                        (long long)batch, (long long)dim);
+  return SSCAN_OK;
+}
+
+int fwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype, const void* x,
+             const void* delta, const float* A, const void* B, const void* C, const float* D, const void* z,
+             const float* delta_bias, const float* initial_state, void* y, float* last_state, void* workspace,
+             size_t workspace_bytes, int64_t num_segments, void* stream) {
+  int rc = check_common(batch, dim, dstate, dtype);
+  if (rc) return rc;
+  if (seqlen < 0) return fail(SSCAN_ERR_INVALID_ARG, "negative seqlen %lld", (long long)seqlen);
+  if (num_segments < 0) return fail(SSCAN_ERR_INVALID_ARG, "negative num_segments");
+  const int64_t max_elems = (int64_t(1) << 62) / 8;
+  if (batch > 0 && dim > 0 && seqlen > max_elems / batch / dim)
+    return fail(SSCAN_ERR_INVALID_ARG, "batch*seqlen*dim too large");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t N = dstate;
+  const size_t es = dtype == SSCAN_BF16 ? 2 : 4;
+  const size_t tok = static_cast<size_t>(batch) * seqlen * dim * es;
+  const size_t bc = static_cast<size_t>(batch) * seqlen * N * es;
+  const size_t st = static_cast<size_t>(batch) * dim * N * sizeof(float);
+  if (batch == 0 || dim == 0) return ok();
+
+  if (seqlen == 0) {
+    if (last_state) {
+      if (initial_state && !aligned(initial_state, 4)) return fail(SSCAN_ERR_INVALID_ARG, "initial_state misaligned");
+      if (!aligned(last_state, 4)) return fail(SSCAN_ERR_INVALID_ARG, "last_state misaligned");
+      if (initial_state != last_state) {
+        if (overlaps(initial_state, st, last_state, st))
+          return fail(SSCAN_ERR_INVALID_ARG, "initial_state and last_state partially overlap");
+        hipError_t e = sscan::launch_fill_state(last_state, initial_state, batch * dim * N, s);
+        if (e != hipSuccess) return hip_fail(e, "fill_state launch");
+      }
+    }
+    return ok();
+  }
+
+  if (!x || !delta || !A || !B || !C || !y)
+    return fail(SSCAN_ERR_INVALID_ARG, "null required pointer (x, delta, A, B, C and y are required)");
+  if (!aligned(x, es) || !aligned(delta, es) || !aligned(y, es) || (z && !aligned(z, es)) || !aligned(B, es) ||
+      !aligned(C, es))
+    return fail(SSCAN_ERR_INVALID_ARG, "token tensor not aligned to its element size");
+  if (!aligned(A, 4) || (D && !aligned(D, 4)) || (delta_bias && !aligned(delta_bias, 4)) ||
+      (initial_state && !aligned(initial_state, 4)) || (last_state && !aligned(last_state, 4)) ||
+      (workspace && !aligned(workspace, 4)))
+    return fail(SSCAN_ERR_INVALID_ARG, "float32 tensor not 4-byte aligned");
+  if (overlaps(y, tok, x, tok) || overlaps(y, tok, delta, tok) || overlaps(y, tok, z, tok) || overlaps(y, tok, B, bc) ||
+      overlaps(y, tok, C, bc) || overlaps(y, tok, A, N * dim * 4))
+    return fail(SSCAN_ERR_INVALID_ARG, "y overlaps an input");
+  if (last_state) {
+    if (overlaps(last_state, st, y, tok) || overlaps(last_state, st, x, tok) || overlaps(last_state, st, delta, tok) ||
+        overlaps(last_state, st, z, tok) || overlaps(last_state, st, B, bc) || overlaps(last_state, st, C, bc))
+      return fail(SSCAN_ERR_INVALID_ARG, "last_state overlaps y or an input");
+    if (initial_state && initial_state != last_state && overlaps(initial_state, st, last_state, st))
+      return fail(SSCAN_ERR_INVALID_ARG, "initial_state and last_state partially overlap");
+  }
+
+  const SegPlan pl = plan_segments(batch, seqlen, dim, N, num_segments, workspace_bytes, workspace != nullptr);
+  if (pl.nseg > 1 && overlaps(workspace, seg_workspace_bytes(batch, dim, N, pl.nseg), y, tok))
+    return fail(SSCAN_ERR_INVALID_ARG, "workspace overlaps y");
+
+  sscan::FwdParams p{};
+  p.x = x; p.dt = delta; p.z = z; p.B = B; p.C = C;
+  p.A = A; p.Dskip = D; p.bias = delta_bias;
+  p.y = y; p.h_last = last_state;
+  p.batch = batch; p.L = seqlen; p.dim = dim; p.N = static_cast<int>(N);
+  p.ndtiles = (dim + sscan::kTile - 1) / sscan::kTile;
+  p.seg_len = pl.seg_len; p.nseg = pl.nseg;
+  const bool bf16 = dtype == SSCAN_BF16;
+
+  if (pl.nseg == 1) {
+    p.h_init = initial_state;
+    hipError_t e = sscan::launch_fwd_main(p, bf16, s);
+    if (e != hipSuccess) return hip_fail(e, "scan launch");
+    return ok();
+  }
+
+  const int64_t bdn = batch * dim * N;
+  float* ws = static_cast<float*>(workspace);
+  float* carry = ws;
+  float* agg_h = ws + pl.nseg * bdn;
+  float* agg_s = ws + 2 * pl.nseg * bdn;
+  p.agg_h = agg_h;
+  p.agg_s = agg_s;
+  hipError_t e = sscan::launch_fwd_aggregate(p, bf16, s);
+  if (e != hipSuccess) return hip_fail(e, "segment aggregate launch");
+  e = sscan::launch_fwd_carry(agg_h, agg_s, A, initial_state, carry, batch, dim, static_cast<int>(N), pl.nseg, s);
+  if (e != hipSuccess) return hip_fail(e, "segment carry launch");
+  p.h_init = carry;
+  e = sscan::launch_fwd_main(p, bf16, s);
+  if (e != hipSuccess) return hip_fail(e, "scan launch");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int sscan_version(void) { return SSCAN_VERSION; }
+
+const char* sscan_last_error(void) { return g_last_error.c_str(); }
+
+size_t sscan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype) {
+  (void)dtype;
+  if (batch <= 0 || seqlen <= 0 || dim <= 0 || dstate < 1 || dstate > SSCAN_MAX_DSTATE) return 0;
+  const SegPlan pl = plan_segments(batch, seqlen, dim, dstate, 0, ~size_t(0), true);
+  return seg_workspace_bytes(batch, dim, dstate, pl.nseg);
+}
+
+int sscan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype, const void* x,
+              const void* delta, const float* A, const void* B, const void* C, const float* D, const void* z,
+              const float* delta_bias, const float* initial_state, void* y, float* last_state, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  return fwd_impl(batch, seqlen, dim, dstate, dtype, x, delta, A, B, C, D, z, delta_bias, initial_state, y,
+                  last_state, workspace, workspace_bytes, 0, stream);
+}
+
+int sscan_fwd_segmented(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype, const void* x,
+                        const void* delta, const float* A, const void* B, const void* C, const float* D,
+                        const void* z, const float* delta_bias, const float* initial_state, void* y,
+                        float* last_state, void* workspace, size_t workspace_bytes, int64_t num_segments,
+                        void* stream) {
+  return fwd_impl(batch, seqlen, dim, dstate, dtype, x, delta, A, B, C, D, z, delta_bias, initial_state, y,
+                  last_state, workspace, workspace_bytes, num_segments, stream);
+}
+
+int sscan_step(int64_t batch, int64_t dim, int64_t dstate, int dtype, float* state, const void* x,
+               const void* delta, const float* A, const void* B, const void* C, const float* D, const void* z,
+               const float* delta_bias, void* y, void* stream) {
+  int rc = check_common(batch, dim, dstate, dtype);
+  if (rc) return rc;
+  if (batch == 0 || dim == 0) return ok();
+  if (!state || !x || !delta || !A || !B || !C || !y)
+    return fail(SSCAN_ERR_INVALID_ARG, "null required pointer (state, x, delta, A, B, C and y are required)");
+  const size_t es = dtype == SSCAN_BF16 ? 2 : 4;
+  if (!aligned(x, es) || !aligned(delta, es) || !aligned(y, es) || (z && !aligned(z, es)) || !aligned(B, es) ||
+      !aligned(C, es))
+    return fail(SSCAN_ERR_INVALID_ARG, "token tensor not aligned to its element size");
+  if (!aligned(state, 4) || !aligned(A, 4) || (D && !aligned(D, 4)) || (delta_bias && !aligned(delta_bias, 4)))
+    return fail(SSCAN_ERR_INVALID_ARG, "float32 tensor not 4-byte aligned");
+  const size_t tok = static_cast<size_t>(batch) * dim * es;
+  const size_t st = static_cast<size_t>(batch) * dim * dstate * sizeof(float);
+  const size_t bc = static_cast<size_t>(batch) * dstate * es;
+  if (overlaps(y, tok, x, tok) || overlaps(y, tok, delta, tok) || overlaps(y, tok, z, tok) || overlaps(y, tok, state, st) ||
+      overlaps(y, tok, B, bc) || overlaps(y, tok, C, bc))
+    return fail(SSCAN_ERR_INVALID_ARG, "y overlaps an input or the state");
+  if (overlaps(state, st, x, tok) || overlaps(state, st, delta, tok) || overlaps(state, st, z, tok) ||
+      overlaps(state, st, B, bc) || overlaps(state, st, C, bc) || overlaps(state, st, A, dim * dstate * 4))
+    return fail(SSCAN_ERR_INVALID_ARG, "state overlaps an input");
+  sscan::StepParams p{};
+  p.state = state; p.x = x; p.dt = delta; p.z = z; p.B = B; p.C = C;
+  p.A = A; p.Dskip = D; p.bias = delta_bias; p.y = y;
+  p.batch = batch; p.dim = dim; p.N = static_cast<int>(dstate);
+  hipError_t e = sscan::launch_step(p, dtype == SSCAN_BF16, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "step launch");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,41 @@
+// Device helpers for the selective-scan kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sscan {
+
+typedef uint16_t bf16_t;  // bfloat16 storage word
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16_t v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
+
+// float32 -> storage type; bf16 uses the hardware round-to-nearest-even convert.
+__device__ __forceinline__ void store_val(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_val(bf16_t* p, float v) { *p = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v)); }
+
+// Hardware transcendentals: 2^x, log2(x), 1/x (each 1 ulp on CDNA).
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// Delta * log2(e) where Delta = softplus(v) = log(1 + e^v), given v2 = v * log2(e).
+// softplus(v) = max(v, 0) + log(1 + e^{-|v|}).  The small term uses u = 1 + w rounded
+// and its exact rounding error r = (u - 1) - w:  log2(1 + w) = log2(u) - r log2(e) / u
+// to first order, and u is close to 1 whenever r matters, so the 1/u factor is dropped.
+__device__ __forceinline__ float softplus_log2e(float v2) {
+  const float m = fmaxf(v2, 0.f);
+  const float w = hw_exp2(-fabsf(v2));
+  const float u = 1.f + w;
+  const float r = (u - 1.f) - w;
+  return m + fmaf(-r, kLog2e, hw_log2(u));
+}
+
+// silu(z) = z * sigmoid(z) = z / (1 + e^{-z}).
+__device__ __forceinline__ float silu(float z) { return z * hw_rcp(1.f + hw_exp2(-z * kLog2e)); }
+
+}  // namespace sscan

@@ -1,0 +1,124 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared entry
+point, and rejects bad arguments on the host before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "selscan.h")
+LIB = os.path.join(ROOT, "selective_state_space_45_amd", "libselscan.so")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from selective_state_space_45_amd import build as b
+        b.build()
+    lb = ctypes.CDLL(LIB)
+    P, I64, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    lb.sscan_fwd.argtypes = [I64, I64, I64, I64, ctypes.c_int] + [P] * 11 + [P, SZ, P]
+    lb.sscan_fwd_segmented.argtypes = [I64, I64, I64, I64, ctypes.c_int] + [P] * 11 + [P, SZ, I64, P]
+    lb.sscan_step.argtypes = [I64, I64, I64, ctypes.c_int] + [P] * 11
+    lb.sscan_last_error.restype = ctypes.c_char_p
+    lb.sscan_fwd_workspace_size.argtypes = [I64, I64, I64, I64, ctypes.c_int]
+    lb.sscan_fwd_workspace_size.restype = SZ
+    return lb
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(sscan_[a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for must in ("sscan_fwd", "sscan_step", "sscan_fwd_segmented", "sscan_fwd_workspace_size",
+                 "sscan_last_error", "sscan_version"):
+        assert must in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version(lib):
+    text = open(HEADER).read()
+    v = int(re.search(r"#define SSCAN_VERSION (\d+)", text).group(1))
+    assert lib.sscan_version() == v
+
+
+FAKE = ctypes.c_void_p(0x10000)      # never dereferenced: every call below fails validation first
+FAKE2 = ctypes.c_void_p(0x20000)
+
+
+def fwd(lib, batch=2, L=8, dim=4, N=4, dtype=0, x=FAKE, dt=FAKE2, A=ctypes.c_void_p(0x30000),
+        B=ctypes.c_void_p(0x40000), C=ctypes.c_void_p(0x50000), D=None, z=None, bias=None, h0=None,
+        y=ctypes.c_void_p(0x60000), hl=None):
+    return lib.sscan_fwd(batch, L, dim, N, dtype, x, dt, A, B, C, D, z, bias, h0, y, hl, None, 0, None)
+
+
+@pytest.mark.parametrize("N", [0, 17, -1])
+def test_dstate_outside_range_is_unsupported(lib, N):
+    assert fwd(lib, N=N) == 2
+    assert b"dstate" in lib.sscan_last_error()
+
+
+def test_unknown_dtype_is_unsupported(lib):
+    assert fwd(lib, dtype=7) == 2
+
+
+@pytest.mark.parametrize("kw", [dict(batch=-1), dict(L=-3), dict(dim=-2)])
+def test_negative_sizes_are_invalid(lib, kw):
+    assert fwd(lib, **kw) == 1
+
+
+@pytest.mark.parametrize("name", ["x", "dt", "A", "B", "C", "y"])
+def test_null_required_pointer_is_invalid(lib, name):
+    assert fwd(lib, **{name: None}) == 1
+    assert b"null" in lib.sscan_last_error()
+
+
+def test_output_overlapping_input_is_invalid(lib):
+    # y starts inside x's byte range
+    assert fwd(lib, x=ctypes.c_void_p(0x100000), y=ctypes.c_void_p(0x100010)) == 1
+    assert b"overlap" in lib.sscan_last_error()
+
+
+def test_misaligned_tensor_is_invalid(lib):
+    assert fwd(lib, dtype=0, x=ctypes.c_void_p(0x10002)) == 1
+    assert b"align" in lib.sscan_last_error()
+
+
+def test_empty_problems_are_noops(lib):
+    assert fwd(lib, batch=0) == 0
+    assert fwd(lib, dim=0) == 0
+    assert fwd(lib, L=0) == 0          # no last_state requested: nothing to do
+    assert lib.sscan_last_error() == b""
+
+
+def test_step_validation(lib):
+    P = ctypes.c_void_p
+    args = [P(0x10000), P(0x20000), P(0x30000), P(0x40000), P(0x50000), P(0x60000), None, None, None, P(0x70000), None]
+    assert lib.sscan_step(4, 8, 17, 0, *args) == 2
+    assert lib.sscan_step(4, 8, 4, 0, None, *args[1:]) == 1
+    assert lib.sscan_step(0, 8, 4, 0, *args) == 0
+
+
+def test_segmented_rejects_negative_segment_count(lib):
+    P = ctypes.c_void_p
+    rc = lib.sscan_fwd_segmented(2, 8, 4, 4, 0, FAKE, FAKE2, P(0x30000), P(0x40000), P(0x50000), None, None, None,
+                                 None, P(0x60000), None, None, 0, -2, None)
+    assert rc == 1
+
+
+def test_workspace_size(lib):
+    # a shape whose (batch, channel tile) grid fills the chip needs no split
+    assert lib.sscan_fwd_workspace_size(8, 4096, 2048, 16, 1) == 0
+    # a long single-row sequence is split: carry + end state + sums per segment
+    ws = lib.sscan_fwd_workspace_size(1, 131072, 2560, 16, 1)
+    assert ws > 0 and ws % (4 * 2560 * 33) == 0
+    assert lib.sscan_fwd_workspace_size(1, 0, 2560, 16, 1) == 0
