@@ -1,0 +1,179 @@
+"""Benchmark of the selective-scan hot path on one MI355X.
+
+A step is one forward scan (``sscan_fwd``: load, softplus step size, zero-order-hold
+discretization, recurrence, readout, skip term, gate, store, final state) over one
+batch of the training-shape workload: batch 8, seqlen 4096, dim 2048, dstate 16,
+bf16 x/delta/z/B/C/y, fp32 A/D/bias/state.  Inputs are resident in HBM before the
+timed region.  One JSON line is printed.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0                       # MI355X HBM3E
+# VALU issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz fp32 lane-operations per second
+# (packed FP32 disabled in this build, so one fp32 op per lane per cycle).
+PEAK_VALU_TOPS = 256 * 64 * 2.4e9 / 1e12
+# Algorithmic VALU operations (an exp/log/rcp counts 2: half-rate on CDNA4):
+OPS_PER_STATE_UPDATE = 8     # Delta*A, exp (2), B/A scale, x scale, add, fma (state), fma (readout)
+OPS_PER_TOKEN_CHANNEL = 20   # softplus 11, silu 7, skip + gate 2
+PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "sscan_fwd_train_shape_counters.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_45_amd", "csrc", f)
+                  for f in ("sscan_fwd.hip", "sscan_device.h", "sscan_internal.h")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(per_launch_units: str = "bytes"):
+    """HBM bytes per launch from committed counter runs, or None if absent or stale."""
+    try:
+        with open(PROFILE_SUMMARY) as f:
+            prof = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if prof.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return prof.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline leg")
+    ap.add_argument("--decode-steps", type=int, default=100)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build runs the scan on a single device "
+              "(multi-GPU sharding is a design note, not implemented); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import selective_state_space_45_amd as ss
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = W.workload("train_shape")
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(torch.bfloat16)
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+    x, dt, z, B, C = bf(w.x), bf(w.dt), bf(w.z), bf(w.B), bf(w.C)
+    A, D, bias = f32(w.A), f32(w.D), f32(w.dt_bias)
+    y = torch.empty_like(x)
+    st = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev)
+    wsb = ss.fwd_workspace_size(w.batch, w.seqlen, w.dim, w.dstate, torch.bfloat16)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        ss.sscan_fwd(x, dt, A, B, C, D=D, z=z, delta_bias=bias, out=y, last_state=st, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # per-launch HIP events on the stream the kernels run on (torch's current stream)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record()
+        step()
+        e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    ms_per_step = wall * 1e3 / args.steps
+    kern_ms = float(np.mean(launch_ms))
+
+    nbytes = W.fwd_algorithmic_bytes(w.batch, w.seqlen, w.dim, w.dstate, "bf16")
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    tokch = w.batch * w.seqlen * w.dim
+    ops = tokch * w.dstate * OPS_PER_STATE_UPDATE + tokch * OPS_PER_TOKEN_CHANNEL
+    achieved_tops = ops / (kern_ms * 1e-3) / 1e12
+    kern_gbs = nbytes / (kern_ms * 1e-3) / 1e9
+
+    # decode step (sscan_step) on the decode workload: reported alongside
+    dw = W.DecodeWorkload()
+    tk = dw.token(0)
+    sd = f32(dw.state0)
+    tx, tdt, tz, tB, tC = bf(tk.x), bf(tk.dt), bf(tk.z), bf(tk.B), bf(tk.C)
+    dA, dD = f32(dw.A), f32(dw.D)
+    yd = torch.empty_like(tx)
+    for _ in range(5):
+        ss.sscan_step(sd, tx, tdt, dA, tB, tC, D=dD, z=tz, out=yd)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.decode_steps):
+        ss.sscan_step(sd, tx, tdt, dA, tB, tC, D=dD, z=tz, out=yd)
+    e1.record()
+    torch.cuda.synchronize()
+    dec_ms = e0.elapsed_time(e1) / args.decode_steps
+    dec_bytes = W.step_algorithmic_bytes(dw.batch, dw.dim, dw.dstate, "bf16")
+
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        rows = 2  # bounded sample: batch rows 0-1 of the same workload, all channels and steps
+        t0 = time.perf_counter()
+        oracle.sscan_fwd(w.x[:rows], w.dt[:rows], w.A, w.B[:rows], w.C[:rows], D=w.D, z=w.z[:rows],
+                         dt_bias=w.dt_bias)
+        cpu_s = time.perf_counter() - t0
+        sample_bytes = W.fwd_algorithmic_bytes(rows, w.seqlen, w.dim, w.dstate, "bf16")
+        cpu = {"value": round(sample_bytes / cpu_s / 1e9, 4), "unit": "GB/s", "cores": oracle.last_threads_used(),
+               "kind": "oracle",
+               "sample": f"batch rows 0-{rows - 1} of the training-shape workload (L=4096, D=2048, N=16), "
+                         f"fp64 sequential recurrence, {cpu_s:.2f} s wall",
+               "tokens_channels_per_s": round(rows * w.seqlen * w.dim / cpu_s, 1)}
+
+    out = {
+        "metric": "selective-scan fwd GB/s effective + % of HBM peak (B=8,L=4096,D=2048,N=16)",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "train_shape: batch 8, seqlen 4096, dim 2048, dstate 16; bf16 x/delta/z/B/C/y, "
+                               "fp32 A/D/delta_bias/state; A=-(n+1), Delta~logU[1e-3,1e-1]; z gate on; "
+                               "final state returned",
+                   "io_dtype": "bf16", "state_dtype": "f32", "segments": 1 if wsb == 0 else "auto"},
+        "hbm_frac_of_peak": round(value / PEAK_HBM_GBS, 4),
+        "tokens_channels_per_s": round(tokch / (ms_per_step * 1e-3), 1),
+        "roofline": {"bound": "alu", "achieved": round(achieved_tops, 3), "peak": round(PEAK_VALU_TOPS, 3),
+                     "unit": "Top/s", "frac": round(achieved_tops / PEAK_VALU_TOPS, 4),
+                     "traffic": measured_traffic(),
+                     "kernel": "fwd_kernel<bf16, 8 waves, main, paired B/C>",
+                     "kernel_ms": round(kern_ms, 5), "kernel_gbs": round(kern_gbs, 2),
+                     "algorithmic_bytes": nbytes, "algorithmic_ops": ops},
+        "decode": {"op": "sscan_step", "workload": "batch 256, dim 5120, dstate 16, bf16 token, fp32 state",
+                   "us_per_step": round(dec_ms * 1e3, 2), "gbs": round(dec_bytes / (dec_ms * 1e-3) / 1e9, 2),
+                   "hbm_frac_of_peak": round(dec_bytes / (dec_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

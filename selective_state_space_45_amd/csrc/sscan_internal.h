@@ -30,6 +30,13 @@ struct FwdParams {
   int nseg;
 };
 
+// Sizes passed by value to the forward kernels (pointers go as separate
+// restrict-qualified arguments so the compiler can keep B/C loads scalar).
+struct FwdShape {
+  int64_t batch, L, dim, seg_len, ndtiles;
+  int N, nseg;
+};
+
 struct StepParams {
   float* state;
   const void* x;
