@@ -5,103 +5,145 @@
 //   Delta = softplus(dt + bias), Abar = exp(Delta A), Bbar = (Abar - 1)/A * B
 //   (Delta * B when A == 0), h <- Abar h + Bbar x (in place), y = (C . h + D x) silu(z).
 //
-// The step is bound by reading and writing the fp32 state [batch, dim, N].
-// LPR lanes share one (b, d) row and each holds 4 consecutive states, so the
-// state is read and written with fully coalesced 16-byte accesses; the partial
-// C . h of the row is summed across its lanes with cross-lane shuffles.
+// The step is bound by reading and writing the fp32 state [batch, dim, N].  Each
+// lane holds 8 (or 4) consecutive states of one (b, d) row, read and written with
+// 16-byte accesses; the partial C . h of a row is summed across its lanes with
+// cross-lane shuffles.
 #include "sscan_device.h"
 #include "sscan_internal.h"
 
 namespace sscan {
 
-template <typename Tin, int LPR, bool VEC>
-__global__ __launch_bounds__(256) void step_kernel(StepParams p) {
-  const Tin* __restrict__ X = static_cast<const Tin*>(p.x);
-  const Tin* __restrict__ DT = static_cast<const Tin*>(p.dt);
-  const Tin* __restrict__ Z = static_cast<const Tin*>(p.z);
-  const Tin* __restrict__ Bp = static_cast<const Tin*>(p.B);
-  const Tin* __restrict__ Cp = static_cast<const Tin*>(p.C);
-  Tin* __restrict__ Y = static_cast<Tin*>(p.y);
-  float* __restrict__ S = p.state;
+// Four consecutive B or C values of one batch row.
+template <typename Tin, bool V>
+__device__ __forceinline__ void load4(const Tin* __restrict__ p, int n0, int N, float* v) {
+  if constexpr (V && sizeof(Tin) == 2) {
+    const uint2 w = *reinterpret_cast<const uint2*>(p);
+    v[0] = __uint_as_float(w.x << 16);
+    v[1] = __uint_as_float(w.x & 0xffff0000u);
+    v[2] = __uint_as_float(w.y << 16);
+    v[3] = __uint_as_float(w.y & 0xffff0000u);
+  } else if constexpr (V) {
+    const float4 f = *reinterpret_cast<const float4*>(p);
+    v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = (n0 + j < N) ? to_f32(p[j]) : 0.f;
+  }
+}
 
-  const int64_t rows = p.batch * p.dim;
+// SPL states per lane (4 or 8), LPR = ceil(N / SPL) lanes per (b, d) row.  VEC: N is a
+// multiple of 4 and state, A, B, C allow 16-byte (8-byte for bf16 B/C) accesses.
+// NFIX: N as a compile-time constant (0 = run time).
+template <typename Tin, int SPL, int LPR, bool VEC, int NFIX>
+__global__ __launch_bounds__(256) void step_kernel(float* __restrict__ S, const Tin* __restrict__ X,
+                                                   const Tin* __restrict__ DT, const Tin* __restrict__ Z,
+                                                   const Tin* __restrict__ Bp, const Tin* __restrict__ Cp,
+                                                   const float* __restrict__ Ag, const float* __restrict__ Dg,
+                                                   const float* __restrict__ biasg, Tin* __restrict__ Y, int64_t rows,
+                                                   int64_t dim, int Nrt) {
+  const int N = NFIX > 0 ? NFIX : Nrt;
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int64_t row = gid / LPR;
   const int q = static_cast<int>(gid - row * LPR);
-  const bool rvalid = row < rows;
-  const int64_t rr = rvalid ? row : 0;
-  const int64_t b = rr / p.dim, d = rr - b * p.dim;
-  const int N = p.N;
-  const int n0 = 4 * q;
+  if (row >= rows) return;  // whole rows leave together: LPR divides the wave size
+  const int64_t b = row / dim, d = row - b * dim;
+  const int n0 = SPL * q;
 
-  float yp = 0.f, xv = 0.f;
-  if (rvalid) {
-    xv = to_f32(X[rr]);
-    const float v2 = fmaf(to_f32(DT[rr]), kLog2e, p.bias ? p.bias[d] * kLog2e : 0.f);
-    const float d2 = softplus_log2e(v2);  // Delta * log2(e)
-    const float* Ad = p.A + d * N + n0;
-    float* Sd = S + rr * N + n0;
-    const Tin* Bb = Bp + b * N + n0;
-    const Tin* Cb = Cp + b * N + n0;
-    float h[4] = {0.f, 0.f, 0.f, 0.f}, a[4] = {0.f, 0.f, 0.f, 0.f};
-    if (VEC && n0 < N) {
-      const float4 hv = *reinterpret_cast<const float4*>(Sd);
-      const float4 av = *reinterpret_cast<const float4*>(Ad);
-      h[0] = hv.x; h[1] = hv.y; h[2] = hv.z; h[3] = hv.w;
-      a[0] = av.x; a[1] = av.y; a[2] = av.z; a[3] = av.w;
-    } else {
+  float yp = 0.f;
+  const float xv = to_f32(X[row]);
+  if (n0 < N) {
+    const float v2 = fmaf(to_f32(DT[row]), kLog2e, biasg ? biasg[d] * kLog2e : 0.f);
+    float h[SPL], a[SPL], bv[SPL], cv[SPL];
+    float* Sd = S + row * N + n0;
+    const float* Ad = Ag + d * N + n0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (n0 + j < N) { h[j] = Sd[j]; a[j] = Ad[j]; }
-    }
+    for (int k = 0; k < SPL / 4; ++k) {
+      if constexpr (VEC) {
+        const float4 hv = *reinterpret_cast<const float4*>(Sd + 4 * k);
+        const float4 av = *reinterpret_cast<const float4*>(Ad + 4 * k);
+        h[4 * k] = hv.x; h[4 * k + 1] = hv.y; h[4 * k + 2] = hv.z; h[4 * k + 3] = hv.w;
+        a[4 * k] = av.x; a[4 * k + 1] = av.y; a[4 * k + 2] = av.z; a[4 * k + 3] = av.w;
+      } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (n0 + j < N) {
-        const float e = hw_exp2(d2 * a[j]);
-        const float g = (a[j] != 0.f) ? (e - 1.f) / a[j] : d2 * kLn2;
-        h[j] = fmaf(e, h[j], g * to_f32(Bb[j]) * xv);
-        yp = fmaf(to_f32(Cb[j]), h[j], yp);
+        for (int j = 4 * k; j < 4 * k + 4; ++j) {
+          h[j] = (n0 + j < N) ? Sd[j] : 0.f;
+          a[j] = (n0 + j < N) ? Ad[j] : 0.f;
+        }
       }
+      load4<Tin, VEC>(Bp + b * N + n0 + 4 * k, n0 + 4 * k, N, bv + 4 * k);
+      load4<Tin, VEC>(Cp + b * N + n0 + 4 * k, n0 + 4 * k, N, cv + 4 * k);
     }
-    if (VEC && n0 < N) {
-      *reinterpret_cast<float4*>(Sd) = make_float4(h[0], h[1], h[2], h[3]);
-    } else {
+    const float d2 = softplus_log2e(v2);  // Delta * log2(e)
+    const float dl = d2 * kLn2;           // Delta
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (n0 + j < N) Sd[j] = h[j];
+    for (int j = 0; j < SPL; ++j) {
+      const float e = hw_exp2(d2 * a[j]);
+      // (Abar - 1) / A, or Delta in the limit A = 0
+      const float g = (a[j] != 0.f) ? (e - 1.f) * hw_rcp(a[j]) : dl;
+      h[j] = fmaf(e, h[j], g * bv[j] * xv);
+      yp = fmaf(cv[j], h[j], yp);
+    }
+#pragma unroll
+    for (int k = 0; k < SPL / 4; ++k) {
+      if constexpr (VEC) {
+        *reinterpret_cast<float4*>(Sd + 4 * k) = make_float4(h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]);
+      } else {
+#pragma unroll
+        for (int j = 4 * k; j < 4 * k + 4; ++j)
+          if (n0 + j < N) Sd[j] = h[j];
+      }
     }
   }
 #pragma unroll
   for (int off = 1; off < LPR; off <<= 1) yp += __shfl_xor(yp, off);
-  if (rvalid && q == 0) {
-    float yv = yp + (p.Dskip ? p.Dskip[d] * xv : 0.f);
-    if (Z) yv *= silu(to_f32(Z[rr]));
-    store_val(&Y[rr], yv);
+  if (q == 0) {
+    float yv = yp + (Dg ? Dg[d] * xv : 0.f);
+    if (Z) yv *= silu(to_f32(Z[row]));
+    store_val(&Y[row], yv);
   }
 }
+
+namespace {
+
+template <typename Tin, int SPL, int LPR, bool VEC, int NF>
+void launch_step_one(const StepParams& p, hipStream_t s) {
+  const int64_t rows = p.batch * p.dim;
+  const int64_t threads = rows * LPR;
+  hipLaunchKernelGGL((step_kernel<Tin, SPL, LPR, VEC, NF>), dim3(static_cast<unsigned>((threads + 255) / 256)),
+                     dim3(256), 0, s, p.state, static_cast<const Tin*>(p.x), static_cast<const Tin*>(p.dt),
+                     static_cast<const Tin*>(p.z), static_cast<const Tin*>(p.B), static_cast<const Tin*>(p.C), p.A,
+                     p.Dskip, p.bias, static_cast<Tin*>(p.y), rows, p.dim, p.N);
+}
+
+template <typename Tin>
+void launch_step_t(const StepParams& p, bool vec, hipStream_t s) {
+  if (p.N == 16 && vec) {
+    launch_step_one<Tin, 8, 2, true, 16>(p, s);  // 8 states per lane
+  } else if (vec) {
+    if (p.N <= 4) launch_step_one<Tin, 4, 1, true, 0>(p, s);
+    else if (p.N <= 8) launch_step_one<Tin, 8, 1, true, 0>(p, s);
+    else launch_step_one<Tin, 8, 2, true, 0>(p, s);
+  } else {
+    if (p.N <= 4) launch_step_one<Tin, 4, 1, false, 0>(p, s);
+    else if (p.N <= 8) launch_step_one<Tin, 8, 1, false, 0>(p, s);
+    else launch_step_one<Tin, 8, 2, false, 0>(p, s);
+  }
+}
+
+}  // namespace
 
 hipError_t launch_step(const StepParams& p, bool bf16, hipStream_t s) {
   const int64_t rows = p.batch * p.dim;
   if (rows <= 0) return hipSuccess;
-  const int lpr = (p.N <= 4) ? 1 : (p.N <= 8 ? 2 : 4);
+  const uintptr_t bcal = bf16 ? 7 : 15;
   const bool vec = (p.N % 4 == 0) && ((reinterpret_cast<uintptr_t>(p.state) & 15) == 0) &&
-                   ((reinterpret_cast<uintptr_t>(p.A) & 15) == 0);
-  const int64_t threads = rows * lpr;
-  const dim3 grid(static_cast<unsigned>((threads + 255) / 256)), block(256);
-#define SSCAN_STEP(TIN, LP, V) hipLaunchKernelGGL((step_kernel<TIN, LP, V>), grid, block, 0, s, p)
-#define SSCAN_STEP_LPR(TIN, V)       \
-  switch (lpr) {                     \
-    case 1: SSCAN_STEP(TIN, 1, V); break; \
-    case 2: SSCAN_STEP(TIN, 2, V); break; \
-    default: SSCAN_STEP(TIN, 4, V); break; \
-  }
-  if (bf16) {
-    if (vec) { SSCAN_STEP_LPR(bf16_t, true) } else { SSCAN_STEP_LPR(bf16_t, false) }
-  } else {
-    if (vec) { SSCAN_STEP_LPR(float, true) } else { SSCAN_STEP_LPR(float, false) }
-  }
-#undef SSCAN_STEP_LPR
-#undef SSCAN_STEP
+                   ((reinterpret_cast<uintptr_t>(p.A) & 15) == 0) && ((reinterpret_cast<uintptr_t>(p.B) & bcal) == 0) &&
+                   ((reinterpret_cast<uintptr_t>(p.C) & bcal) == 0);
+  if (bf16)
+    launch_step_t<bf16_t>(p, vec, s);
+  else
+    launch_step_t<float>(p, vec, s);
   return hipGetLastError();
 }
 
