@@ -8,10 +8,13 @@ timed region.  One JSON line is printed.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
                     [--copy-calibration]
+    python bench.py --summarize-counters FETCH_CSV WRITE_CSV   (CPU only)
 
 --copy-calibration also runs a plain 512 MiB -> 512 MiB elementwise copy (three
 times), the known-size reference that scales the HBM byte counters read by
-rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE.
+rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE.  --summarize-counters turns the two
+counter CSVs into profiles/sscan_fwd_train_shape_counters.json, from which
+roofline.traffic is reported while the kernel sources are unchanged.
 """
 import argparse
 import hashlib
@@ -36,10 +39,16 @@ KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_45_amd", "csrc", f)
 
 
 def kernel_source_hash() -> str:
+    """Hash of the forward kernel's code, comments and blank space removed (so an
+    edited comment does not mark the counter figures stale; any code change does)."""
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f) as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 
@@ -55,7 +64,51 @@ def measured_traffic(per_launch_units: str = "bytes"):
     return prof.get("hbm_bytes_per_launch")
 
 
+def summarize_counters(fetch_csv: str, write_csv: str) -> dict:
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, both with
+    --copy-calibration) into the per-launch HBM traffic of the forward kernel.
+
+    Each counter is scaled by the factor that maps its reading on the calibration
+    copy (512 MiB read, 512 MiB written) to those true byte counts.  CPU only."""
+    import csv
+
+    def per_kernel(path, counter):
+        acc = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in acc.items()}
+
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    pick = lambda tab, key: next(v for k, v in tab.items() if key in k)
+    copy_bytes = 512 * 1024 * 1024
+    ff = copy_bytes / (pick(fetch, "AUnaryFunctor") * 1024)
+    fw = copy_bytes / (pick(write, "AUnaryFunctor") * 1024)
+    fk, wk = pick(fetch, "sscan::fwd_kernel"), pick(write, "sscan::fwd_kernel")
+    rd, wr = fk * 1024 * ff, wk * 1024 * fw
+    import workloads as W
+    alg = W.fwd_algorithmic_bytes(8, 4096, 2048, 16, "bf16")
+    return {"kernel": next(k for k in fetch if "sscan::fwd_kernel" in k).split("(")[0],
+            "workload": "train_shape: batch 8, seqlen 4096, dim 2048, dstate 16, bf16 io, fp32 state",
+            "kernel_source_hash": kernel_source_hash(),
+            "fetch_size_kib_per_dispatch": round(fk, 1), "write_size_kib_per_dispatch": round(wk, 1),
+            "copy_calibration": {"kernel": "torch elementwise mul by 1, 512 MiB fp32 in -> 512 MiB out",
+                                 "fetch_size_kib": round(pick(fetch, "AUnaryFunctor"), 1),
+                                 "write_size_kib": round(pick(write, "AUnaryFunctor"), 1),
+                                 "fetch_factor": round(ff, 4), "write_factor": round(fw, 4)},
+            "hbm_read_bytes_per_launch": int(round(rd)), "hbm_write_bytes_per_launch": int(round(wr)),
+            "hbm_bytes_per_launch": int(round(rd + wr)), "algorithmic_bytes_per_launch": alg,
+            "traffic_over_algorithmic": round((rd + wr) / alg, 4)}
+
+
 def main():
+    if len(sys.argv) == 4 and sys.argv[1] == "--summarize-counters":
+        out = summarize_counters(sys.argv[2], sys.argv[3])
+        with open(PROFILE_SUMMARY, "w") as f:
+            json.dump(out, f, indent=1)
+        print(json.dumps(out, indent=1))
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)

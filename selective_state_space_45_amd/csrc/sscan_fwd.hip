@@ -6,18 +6,19 @@
 // h_l = Abar h_{l-1} + Bbar x_l, y_l = (C_l . h_l + D x_l) * silu(z_l).
 //
 // Work decomposition.  A workgroup owns one (batch row, 64-channel tile, sequence
-// segment).  Its NSPLIT waves split the N states, two states per wave, so the
-// whole state of a channel stays in registers but spread over waves, and each
-// lane of a wave is one channel.  The sequence is consumed in chunks of kChunk
+// segment).  Its NSPLIT waves split the N states, one state per wave (NSPLIT is N
+// rounded up to a power of two), so the whole state of a channel stays in
+// registers but spread over waves, and each lane of a wave is one channel.  The sequence is consumed in chunks of kChunk
 // timesteps, software-pipelined with one barrier per chunk:
 //   prologue   x, dt, z loaded coalesced along channels (each (l, d) once per
 //              workgroup), Delta*log2(e) and x staged to LDS, silu(z) and D*x
 //              kept in registers for the epilogue;
-//   recurrence each wave reads (Delta, x) from LDS, B and C of its two states
-//              arrive through scalar loads (uniform across the wave), updates its
-//              states and writes a partial C.h to LDS;
-//   epilogue   partials of all waves are summed, skip term and gate applied, y
-//              stored coalesced.
+//   recurrence each wave reads (Delta, x) from LDS, the B value of its state
+//              arrives through scalar loads (uniform across the wave), and the
+//              state after every timestep is written to LDS;
+//   epilogue   each wave reads back all N states of its own prologue timesteps,
+//              forms C.h with the C row (scalar loads), adds the skip term,
+//              applies the gate and stores y coalesced.
 // The state update uses h <- Abar (h + k) - k with k = x B / A, which equals
 // Abar h + (Abar - 1) B x / A = Abar h + Bbar x: one add and one fma per state.
 // A wave whose channels have some A == 0 switches to the explicit form with the

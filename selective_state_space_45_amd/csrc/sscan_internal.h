@@ -52,7 +52,7 @@ struct StepParams {
   int N;
 };
 
-// Waves per workgroup of the forward kernels for a given N (each wave owns 2 states).
+// Waves per workgroup of the forward kernels for a given N (each wave owns one state).
 int fwd_nsplit(int N);
 
 // Launchers; return hipSuccess or the launch error.
