@@ -7,7 +7,7 @@ bf16 x/delta/z/B/C/y, fp32 A/D/bias/state.  Inputs are resident in HBM before th
 timed region.  One JSON line is printed.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
-                    [--copy-calibration]
+                    [--no-euler] [--copy-calibration]
     python bench.py --summarize-counters FETCH_CSV WRITE_CSV   (CPU only)
 
 --copy-calibration also runs a plain 512 MiB -> 512 MiB elementwise copy (three
@@ -82,14 +82,17 @@ def summarize_counters(fetch_csv: str, write_csv: str) -> dict:
 
     fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
     pick = lambda tab, key: next(v for k, v in tab.items() if key in k)
+    # the zero-order-hold forward kernel: its last template argument (EULER) is false
+    zoh = lambda k: "sscan::fwd_kernel<" in k and k.split("(")[0].endswith("false>")
     copy_bytes = 512 * 1024 * 1024
     ff = copy_bytes / (pick(fetch, "AUnaryFunctor") * 1024)
     fw = copy_bytes / (pick(write, "AUnaryFunctor") * 1024)
-    fk, wk = pick(fetch, "sscan::fwd_kernel"), pick(write, "sscan::fwd_kernel")
+    fk = next(v for k, v in fetch.items() if zoh(k))
+    wk = next(v for k, v in write.items() if zoh(k))
     rd, wr = fk * 1024 * ff, wk * 1024 * fw
     import workloads as W
     alg = W.fwd_algorithmic_bytes(8, 4096, 2048, 16, "bf16")
-    return {"kernel": next(k for k in fetch if "sscan::fwd_kernel" in k).split("(")[0],
+    return {"kernel": next(k for k in fetch if zoh(k)).split("(")[0],
             "workload": "train_shape: batch 8, seqlen 4096, dim 2048, dstate 16, bf16 io, fp32 state",
             "kernel_source_hash": kernel_source_hash(),
             "fetch_size_kib_per_dispatch": round(fk, 1), "write_size_kib_per_dispatch": round(wk, 1),
@@ -115,6 +118,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline leg")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step leg")
+    ap.add_argument("--no-euler", action="store_true", help="skip the Euler-rule leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 512 MiB elementwise copy (counter calibration)")
     ap.add_argument("--decode-steps", type=int, default=100)
@@ -168,6 +172,29 @@ def main():
     ops = tokch * w.dstate * OPS_PER_STATE_UPDATE + tokch * OPS_PER_TOKEN_CHANNEL
     achieved_tops = ops / (kern_ms * 1e-3) / 1e12
     kern_gbs = nbytes / (kern_ms * 1e-3) / 1e9
+
+    # the Euler rule (Bbar = Delta B) on the same workload, reported alongside
+    def timed_launches(fn, n):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for e0, e1 in ev:
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        return float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+
+    def step_euler():
+        ss.sscan_fwd(x, dt, A, B, C, D=D, z=z, delta_bias=bias, out=y, last_state=st, workspace=ws, euler=True)
+
+    euler = None
+    if not args.no_euler:
+        for _ in range(3):
+            step_euler()
+        torch.cuda.synchronize()
+        eu_ms = timed_launches(step_euler, max(5, args.steps // 2))
+        euler = {"op": "sscan_fwd, Euler rule (flag SSCAN_FLAG_EULER)", "kernel_ms": round(eu_ms, 5),
+                 "gbs": round(nbytes / (eu_ms * 1e-3) / 1e9, 2),
+                 "hbm_frac_of_peak": round(nbytes / (eu_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 
     # decode step (sscan_step) on the decode workload, reported alongside.  The steps
     # are captured in a HIP graph and replayed, so host-side launch overhead is not
@@ -255,6 +282,7 @@ def main():
                      "kernel": "fwd_kernel<bf16, 16 waves x 1 state, main, paired B/C, N=16>",
                      "kernel_ms": round(kern_ms, 5), "kernel_gbs": round(kern_gbs, 2),
                      "algorithmic_bytes": nbytes, "algorithmic_ops": ops},
+        "euler": euler,
         "decode": decode,
         "cpu_baseline": cpu,
     }

@@ -36,6 +36,8 @@
  *    Inf propagate.  SSCAN_ERR_HIP reports a failed launch.
  *  - Outputs must not overlap inputs, except where stated (in-place state).
  *  - dstate (N) must be in [1, SSCAN_MAX_DSTATE].
+ *  - `flags` selects variants of the method (SSCAN_FLAG_*); 0 is the method
+ *    as defined above.
  */
 #ifndef SELSCAN_H
 #define SELSCAN_H
@@ -47,8 +49,19 @@
 extern "C" {
 #endif
 
-#define SSCAN_VERSION 100
+#define SSCAN_VERSION 200
 #define SSCAN_MAX_DSTATE 16
+
+/*
+ * Bits of the `flags` argument.
+ *
+ * SSCAN_FLAG_EULER: discretize B with the first-order (Euler) rule
+ *   Bbar = Delta * B   instead of the zero-order hold (Abar is exp(Delta A) either way).
+ *   This is the rule the page-3 report's code uses (section 4.2,
+ *   selective_scan / selective_scan_seq: deltaB = delta * B, BX = deltaB * x).
+ * Unknown bits are rejected with SSCAN_ERR_UNSUPPORTED.
+ */
+#define SSCAN_FLAG_EULER 1u
 
 typedef enum {
   SSCAN_OK = 0,
@@ -96,7 +109,7 @@ size_t sscan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int6
  * Alignment: dtype-size alignment for token tensors, 4 bytes for float32 ones.
  */
 int sscan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
-              const void* x, const void* delta, const float* A, const void* B, const void* C,
+              unsigned int flags, const void* x, const void* delta, const float* A, const void* B, const void* C,
               const float* D, const void* z, const float* delta_bias,
               const float* initial_state, void* y, float* last_state,
               void* workspace, size_t workspace_bytes, void* stream);
@@ -109,7 +122,7 @@ int sscan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dt
  * up to float32 rounding.
  */
 int sscan_fwd_segmented(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
-                        const void* x, const void* delta, const float* A, const void* B,
+                        unsigned int flags, const void* x, const void* delta, const float* A, const void* B,
                         const void* C, const float* D, const void* z, const float* delta_bias,
                         const float* initial_state, void* y, float* last_state,
                         void* workspace, size_t workspace_bytes, int64_t num_segments,
@@ -127,7 +140,7 @@ int sscan_fwd_segmented(int64_t batch, int64_t seqlen, int64_t dim, int64_t dsta
  * Optional (NULL allowed): D, z, delta_bias.  Equivalent to sscan_fwd with
  * seqlen = 1, initial_state = last_state = state.
  */
-int sscan_step(int64_t batch, int64_t dim, int64_t dstate, int dtype,
+int sscan_step(int64_t batch, int64_t dim, int64_t dstate, int dtype, unsigned int flags,
                float* state, const void* x, const void* delta, const float* A,
                const void* B, const void* C, const float* D, const void* z,
                const float* delta_bias, void* y, void* stream);

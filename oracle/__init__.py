@@ -21,6 +21,8 @@ What it computes, and the passages it follows (the reference pages):
 * h_k = Abar h_{k-1} + Bbar x_k, y_k = C h_k (+ D x_k), then y * silu(z):
   velog.io review "Discretization" item 3; page-3 report sections 3 and 4.2.
 * Recurrent step on a carried (B, D, N) state: page-3 report section 6 (ssm_step).
+* ``euler=True``: Bbar = Delta B, the first-order rule of the page-3 report's code
+  (section 4.2, ``deltaB = delta * B``).
 
 Parity status: every function here is pinned by the ``-m "not gpu"`` tests in
 ``tests/test_oracle_pins.py`` (closed forms, a hand-derived worked example,
@@ -77,9 +79,9 @@ class Oracle:
         lib = ctypes.CDLL(lib_path)
         P = ctypes.c_void_p
         I64 = ctypes.c_int64
-        lib.oracle_sscan_fwd.argtypes = [I64, I64, I64, I64] + [P] * 11 + [ctypes.c_int]
+        lib.oracle_sscan_fwd.argtypes = [I64, I64, I64, I64, ctypes.c_int] + [P] * 11 + [ctypes.c_int]
         lib.oracle_sscan_fwd.restype = ctypes.c_int
-        lib.oracle_sscan_step.argtypes = [I64, I64, I64] + [P] * 10 + [ctypes.c_int]
+        lib.oracle_sscan_step.argtypes = [I64, I64, I64, ctypes.c_int] + [P] * 10 + [ctypes.c_int]
         lib.oracle_sscan_step.restype = ctypes.c_int
         lib.oracle_nthreads_default.argtypes = []
         lib.oracle_nthreads_default.restype = ctypes.c_int
@@ -90,9 +92,9 @@ class Oracle:
         return int(self.lib.oracle_nthreads_default())
 
     def sscan_fwd(self, x, dt, A, B, C, D=None, z=None, dt_bias=None, h0=None,
-                  return_last_state: bool = True, nthreads: int = 0
+                  return_last_state: bool = True, nthreads: int = 0, euler: bool = False
                   ) -> Tuple[np.ndarray, Optional[np.ndarray]]:
-        """fp64 forward scan.
+        """fp64 forward scan (``euler``: Bbar = Delta B instead of the zero-order hold).
 
         x, dt, z: [batch, seqlen, dim]; A: [dim, dstate]; B, C: [batch, seqlen, dstate];
         D, dt_bias: [dim]; h0: optional initial state [batch, dim, dstate] (zeros if None).
@@ -115,7 +117,7 @@ class Oracle:
         h0 = _f64(h0, (Bt, Dm, N), "h0")
         y = np.empty((Bt, L, Dm), dtype=np.float64)
         hl = np.empty((Bt, Dm, N), dtype=np.float64) if return_last_state else None
-        used = self.lib.oracle_sscan_fwd(Bt, L, Dm, N, _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+        used = self.lib.oracle_sscan_fwd(Bt, L, Dm, N, int(bool(euler)), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
                                          _ptr(D), _ptr(z), _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(hl),
                                          int(nthreads))
         if used < 0:
@@ -123,7 +125,8 @@ class Oracle:
         self.last_threads_used = used
         return y, hl
 
-    def sscan_step(self, state, x, dt, A, B, C, D=None, z=None, dt_bias=None, nthreads: int = 0):
+    def sscan_step(self, state, x, dt, A, B, C, D=None, z=None, dt_bias=None, nthreads: int = 0,
+                   euler: bool = False):
         """fp64 single-token step.  ``state`` [batch, dim, dstate] (float64, C-contiguous)
         is updated in place; x, dt, z: [batch, dim]; B, C: [batch, dstate].  Returns y [batch, dim]."""
         if not (isinstance(state, np.ndarray) and state.dtype == np.float64 and state.flags.c_contiguous):
@@ -138,7 +141,7 @@ class Oracle:
         z = _f64(z, (Bt, Dm), "z")
         dt_bias = _f64(dt_bias, (Dm,), "dt_bias")
         y = np.empty((Bt, Dm), dtype=np.float64)
-        used = self.lib.oracle_sscan_step(Bt, Dm, N, _ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+        used = self.lib.oracle_sscan_step(Bt, Dm, N, int(bool(euler)), _ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
                                           _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias), _ptr(y), int(nthreads))
         if used < 0:
             raise ValueError("oracle_sscan_step rejected its arguments")

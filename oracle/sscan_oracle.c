@@ -17,6 +17,10 @@
  *   y      = sum_n C[b,l,n] * h[n] + Dskip[d] * x[b,l,d]
  *   y     *= z * sigmoid(z)                            (only when z is given)
  *
+ * Variant (euler != 0): Bbar = Delta * B[b,l,n], the first-order rule that the
+ * page-3 report's code uses (section 4.2, selective_scan_seq: deltaB = delta * B);
+ * Abar stays exp(Delta A).
+ *
  * Sources (the reference pages):
  *  - ZOH formulas Abar = exp(Delta A), Bbar = (Delta A)^-1 (exp(Delta A) - I) Delta B:
  *    velog.io Mamba paper review, section "2 State Space Models", "Discretization";
@@ -58,7 +62,7 @@ static double softplus(double v) {
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 
 /* One (b, d) row of the forward scan over all seqlen steps. */
-static void scan_row(int64_t b, int64_t d, int64_t L, int64_t Dm, int64_t N,
+static void scan_row(int64_t b, int64_t d, int64_t L, int64_t Dm, int64_t N, int euler,
                      const double* x, const double* dt, const double* A,
                      const double* Bm, const double* Cm, const double* Dskip,
                      const double* z, const double* bias, const double* h0,
@@ -75,7 +79,7 @@ static void scan_row(int64_t b, int64_t d, int64_t L, int64_t Dm, int64_t N,
       const double an = A[d * N + n];
       const double a = delta * an;
       const double abar = exp(a);
-      const double bbar = (an != 0.0) ? expm1(a) / an * Bm[r + n] : delta * Bm[r + n];
+      const double bbar = (an != 0.0 && !euler) ? expm1(a) / an * Bm[r + n] : delta * Bm[r + n];
       h[n] = abar * h[n] + bbar * xv;
       acc += Cm[r + n] * h[n];
     }
@@ -90,8 +94,9 @@ static void scan_row(int64_t b, int64_t d, int64_t L, int64_t Dm, int64_t N,
 int oracle_nthreads_default(void) { return omp_get_max_threads(); }
 
 /* Forward scan.  h0 may be NULL (zero initial state); h_last may be NULL.
+ * euler != 0 selects Bbar = Delta * B.
  * Returns the number of threads used, or -1 on a bad argument. */
-int oracle_sscan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+int oracle_sscan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int euler,
                      const double* x, const double* dt, const double* A,
                      const double* Bm, const double* Cm, const double* Dskip,
                      const double* z, const double* bias, const double* h0,
@@ -108,7 +113,7 @@ int oracle_sscan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
 #pragma omp for schedule(dynamic, 1)
     for (int64_t rd = 0; rd < rows; ++rd) {
       const int64_t b = rd / dim, d = rd % dim;
-      scan_row(b, d, seqlen, dim, dstate, x, dt, A, Bm, Cm, Dskip, z, bias, h0, y, h_last, h);
+      scan_row(b, d, seqlen, dim, dstate, euler, x, dt, A, Bm, Cm, Dskip, z, bias, h0, y, h_last, h);
     }
   }
   return used;
@@ -117,7 +122,7 @@ int oracle_sscan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
 /* One recurrent step: the forward scan with seqlen = 1, starting from and
  * writing back `state` [batch][dim][dstate].  Token tensors are [batch][dim]
  * and [batch][dstate]. */
-int oracle_sscan_step(int64_t batch, int64_t dim, int64_t dstate, double* state,
+int oracle_sscan_step(int64_t batch, int64_t dim, int64_t dstate, int euler, double* state,
                       const double* x, const double* dt, const double* A,
                       const double* Bm, const double* Cm, const double* Dskip,
                       const double* z, const double* bias, double* y, int nthreads) {
@@ -134,7 +139,7 @@ int oracle_sscan_step(int64_t batch, int64_t dim, int64_t dstate, double* state,
     for (int64_t rd = 0; rd < rows; ++rd) {
       const int64_t b = rd / dim, d = rd % dim;
       /* seqlen = 1: the [B,1,D] and [B,1,N] layouts coincide with [B,D] and [B,N]. */
-      scan_row(b, d, 1, dim, dstate, x, dt, A, Bm, Cm, Dskip, z, bias, state, y, state, h);
+      scan_row(b, d, 1, dim, dstate, euler, x, dt, A, Bm, Cm, Dskip, z, bias, state, y, state, h);
     }
   }
   return used;

@@ -32,14 +32,16 @@ _lib.sscan_last_error.argtypes = []
 _lib.sscan_last_error.restype = ctypes.c_char_p
 _lib.sscan_fwd_workspace_size.argtypes = [_I64, _I64, _I64, _I64, ctypes.c_int]
 _lib.sscan_fwd_workspace_size.restype = _SZ
-_lib.sscan_fwd.argtypes = [_I64, _I64, _I64, _I64, ctypes.c_int] + [_P] * 11 + [_P, _SZ, _P]
+_U32 = ctypes.c_uint
+_lib.sscan_fwd.argtypes = [_I64, _I64, _I64, _I64, ctypes.c_int, _U32] + [_P] * 11 + [_P, _SZ, _P]
 _lib.sscan_fwd.restype = ctypes.c_int
-_lib.sscan_fwd_segmented.argtypes = [_I64, _I64, _I64, _I64, ctypes.c_int] + [_P] * 11 + [_P, _SZ, _I64, _P]
+_lib.sscan_fwd_segmented.argtypes = [_I64, _I64, _I64, _I64, ctypes.c_int, _U32] + [_P] * 11 + [_P, _SZ, _I64, _P]
 _lib.sscan_fwd_segmented.restype = ctypes.c_int
-_lib.sscan_step.argtypes = [_I64, _I64, _I64, ctypes.c_int] + [_P] * 11
+_lib.sscan_step.argtypes = [_I64, _I64, _I64, ctypes.c_int, _U32] + [_P] * 11
 _lib.sscan_step.restype = ctypes.c_int
 
 SSCAN_F32, SSCAN_BF16 = 0, 1
+SSCAN_FLAG_EULER = 1
 _DTYPES = {torch.float32: SSCAN_F32, torch.bfloat16: SSCAN_BF16}
 STATUS = {0: "SSCAN_OK", 1: "SSCAN_ERR_INVALID_ARG", 2: "SSCAN_ERR_UNSUPPORTED", 3: "SSCAN_ERR_HIP"}
 
@@ -97,10 +99,11 @@ def sscan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Te
               delta_bias: Optional[torch.Tensor] = None, initial_state: Optional[torch.Tensor] = None,
               return_last_state: bool = False, out: Optional[torch.Tensor] = None,
               last_state: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-              num_segments: Optional[int] = None):
+              num_segments: Optional[int] = None, euler: bool = False):
     """Forward selective scan.  x, delta, z: [batch, seqlen, dim]; B, C: [batch, seqlen, dstate]
     (all float32 or all bfloat16); A: [dim, dstate], D, delta_bias: [dim], initial_state:
-    [batch, dim, dstate] (float32).  Returns y, or (y, last_state)."""
+    [batch, dim, dstate] (float32).  euler: Bbar = Delta B instead of the zero-order hold.
+    Returns y, or (y, last_state)."""
     if x.dim() != 3:
         raise ValueError("x must be [batch, seqlen, dim]")
     batch, seqlen, dim = x.shape
@@ -134,7 +137,8 @@ def sscan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Te
             need = max(need, 4 * num_segments * batch * dim * (2 * dstate + 1))
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device) if need > 0 else None
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    args = [batch, seqlen, dim, dstate, dt, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+    flags = SSCAN_FLAG_EULER if euler else 0
+    args = [batch, seqlen, dim, dstate, dt, flags, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
             _ptr(delta_bias), _ptr(initial_state), _ptr(y), _ptr(ls), _ptr(workspace), wbytes]
     if num_segments is None:
         _check(_lib.sscan_fwd(*args, _stream(x.device)))
@@ -147,9 +151,11 @@ def sscan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Te
 
 def sscan_step(state: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
                C: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
-               delta_bias: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+               delta_bias: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+               euler: bool = False) -> torch.Tensor:
     """One decode step.  state: [batch, dim, dstate] float32, updated in place; x, delta, z:
-    [batch, dim]; B, C: [batch, dstate] (float32 or bfloat16); A: [dim, dstate].  Returns y [batch, dim]."""
+    [batch, dim]; B, C: [batch, dstate] (float32 or bfloat16); A: [dim, dstate].  euler: Bbar =
+    Delta B instead of the zero-order hold.  Returns y [batch, dim]."""
     if x.dim() != 2:
         raise ValueError("x must be [batch, dim]")
     batch, dim = x.shape
@@ -170,6 +176,6 @@ def sscan_step(state: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, A: tor
         _dev(delta_bias, "delta_bias", torch.float32, (dim,))
     y = out if out is not None else torch.empty_like(x)
     _dev(y, "out", x.dtype, x.shape)
-    _check(_lib.sscan_step(batch, dim, dstate, _DTYPES[x.dtype], _ptr(state), _ptr(x), _ptr(delta), _ptr(A),
+    _check(_lib.sscan_step(batch, dim, dstate, _DTYPES[x.dtype], SSCAN_FLAG_EULER if euler else 0, _ptr(state), _ptr(x), _ptr(delta), _ptr(A),
                            _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(y), _stream(x.device)))
     return y

@@ -22,21 +22,44 @@ def hipcc() -> str:
     return cand if os.path.exists(cand) else "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-I" + os.path.join(ROOT, "include"), "-o", tmp] + \
-        [os.path.join(HERE, s) for s in SOURCES]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if "is not a recognized feature" not in ln
             and "packed-fp32-ops" not in ln and ln.strip()]
-    if res.returncode != 0:
-        sys.stderr.write("\n".join(msgs) + "\n")
-        raise RuntimeError("hipcc failed building libselscan.so")
-    if verbose and msgs:
-        print("\n".join(msgs))
-    os.replace(tmp, LIB)
+    return res.returncode, msgs
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source to an object (in parallel), then link libselscan.so."""
+    from concurrent.futures import ThreadPoolExecutor
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    tag = "%d" % os.getpid()
+    objs = [os.path.join(objdir, os.path.basename(src).replace(".hip", ".%s.o" % tag)) for src in SOURCES]
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    jobs = [[hipcc()] + compile_flags + ["-I" + os.path.join(ROOT, "include"), "-c", "-o", o,
+                                         os.path.join(HERE, src)] for src, o in zip(SOURCES, objs)]
+    try:
+        with ThreadPoolExecutor(max(1, min(len(jobs), os.cpu_count() or 1))) as ex:
+            results = list(ex.map(lambda c: _run(c, verbose), jobs))
+        for (rc, msgs), src in zip(results, SOURCES):
+            if rc != 0:
+                sys.stderr.write("\n".join(msgs) + "\n")
+                raise RuntimeError("hipcc failed compiling %s" % src)
+            if verbose and msgs:
+                print("\n".join(msgs))
+        tmp = LIB + ".tmp" + tag
+        rc, msgs = _run([hipcc()] + HIPCC_FLAGS + ["-o", tmp] + objs, verbose)
+        if rc != 0:
+            sys.stderr.write("\n".join(msgs) + "\n")
+            raise RuntimeError("hipcc failed linking libselscan.so")
+        os.replace(tmp, LIB)
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
     return LIB
 
 

@@ -101,8 +101,9 @@ bool overlaps(const void* a, size_t abytes, const void* b, size_t bbytes) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-int check_common(int64_t batch, int64_t dim, int64_t dstate, int dtype) {
+int check_common(int64_t batch, int64_t dim, int64_t dstate, int dtype, unsigned flags) {
   if (dtype != SSCAN_F32 && dtype != SSCAN_BF16) return fail(SSCAN_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+  if (flags & ~SSCAN_FLAG_EULER) return fail(SSCAN_ERR_UNSUPPORTED, "unknown flag bits 0x%x", flags);
   if (dstate < 1 || dstate > SSCAN_MAX_DSTATE)
     return fail(SSCAN_ERR_UNSUPPORTED, "dstate %lld outside [1, %d]", (long long)dstate, SSCAN_MAX_DSTATE);
   if (batch < 0 || dim < 0) return fail(SSCAN_ERR_INVALID_ARG, "negative size (batch %lld, dim %lld)",
@@ -110,11 +111,11 @@ int check_common(int64_t batch, int64_t dim, int64_t dstate, int dtype) {
   return SSCAN_OK;
 }
 
-int fwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype, const void* x,
+int fwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype, unsigned flags, const void* x,
              const void* delta, const float* A, const void* B, const void* C, const float* D, const void* z,
              const float* delta_bias, const float* initial_state, void* y, float* last_state, void* workspace,
              size_t workspace_bytes, int64_t num_segments, void* stream) {
-  int rc = check_common(batch, dim, dstate, dtype);
+  int rc = check_common(batch, dim, dstate, dtype, flags);
   if (rc) return rc;
   if (seqlen < 0) return fail(SSCAN_ERR_INVALID_ARG, "negative seqlen %lld", (long long)seqlen);
   if (num_segments < 0) return fail(SSCAN_ERR_INVALID_ARG, "negative num_segments");
@@ -174,6 +175,7 @@ int fwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dty
   p.batch = batch; p.L = seqlen; p.dim = dim; p.N = static_cast<int>(N);
   p.ndtiles = (dim + sscan::kTile - 1) / sscan::kTile;
   p.seg_len = pl.seg_len; p.nseg = pl.nseg;
+  p.euler = (flags & SSCAN_FLAG_EULER) != 0;
   const bool bf16 = dtype == SSCAN_BF16;
 
   if (pl.nseg == 1) {
@@ -215,27 +217,27 @@ size_t sscan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int6
   return seg_workspace_bytes(batch, dim, dstate, pl.nseg);
 }
 
-int sscan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype, const void* x,
-              const void* delta, const float* A, const void* B, const void* C, const float* D, const void* z,
-              const float* delta_bias, const float* initial_state, void* y, float* last_state, void* workspace,
-              size_t workspace_bytes, void* stream) {
-  return fwd_impl(batch, seqlen, dim, dstate, dtype, x, delta, A, B, C, D, z, delta_bias, initial_state, y,
+int sscan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype, unsigned int flags,
+              const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
+              const void* z, const float* delta_bias, const float* initial_state, void* y, float* last_state,
+              void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_impl(batch, seqlen, dim, dstate, dtype, flags, x, delta, A, B, C, D, z, delta_bias, initial_state, y,
                   last_state, workspace, workspace_bytes, 0, stream);
 }
 
-int sscan_fwd_segmented(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype, const void* x,
-                        const void* delta, const float* A, const void* B, const void* C, const float* D,
+int sscan_fwd_segmented(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+                        unsigned int flags, const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
                         const void* z, const float* delta_bias, const float* initial_state, void* y,
                         float* last_state, void* workspace, size_t workspace_bytes, int64_t num_segments,
                         void* stream) {
-  return fwd_impl(batch, seqlen, dim, dstate, dtype, x, delta, A, B, C, D, z, delta_bias, initial_state, y,
+  return fwd_impl(batch, seqlen, dim, dstate, dtype, flags, x, delta, A, B, C, D, z, delta_bias, initial_state, y,
                   last_state, workspace, workspace_bytes, num_segments, stream);
 }
 
-int sscan_step(int64_t batch, int64_t dim, int64_t dstate, int dtype, float* state, const void* x,
-               const void* delta, const float* A, const void* B, const void* C, const float* D, const void* z,
-               const float* delta_bias, void* y, void* stream) {
-  int rc = check_common(batch, dim, dstate, dtype);
+int sscan_step(int64_t batch, int64_t dim, int64_t dstate, int dtype, unsigned int flags, float* state,
+               const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
+               const void* z, const float* delta_bias, void* y, void* stream) {
+  int rc = check_common(batch, dim, dstate, dtype, flags);
   if (rc) return rc;
   if (batch == 0 || dim == 0) return ok();
   if (!state || !x || !delta || !A || !B || !C || !y)
@@ -259,6 +261,7 @@ int sscan_step(int64_t batch, int64_t dim, int64_t dstate, int dtype, float* sta
   p.state = state; p.x = x; p.dt = delta; p.z = z; p.B = B; p.C = C;
   p.A = A; p.Dskip = D; p.bias = delta_bias; p.y = y;
   p.batch = batch; p.dim = dim; p.N = static_cast<int>(dstate);
+  p.euler = (flags & SSCAN_FLAG_EULER) != 0;
   hipError_t e = sscan::launch_step(p, dtype == SSCAN_BF16, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "step launch");
   return ok();

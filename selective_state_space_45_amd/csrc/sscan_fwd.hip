@@ -22,7 +22,9 @@
 // The state update uses h <- Abar (h + k) - k with k = x B / A, which equals
 // Abar h + (Abar - 1) B x / A = Abar h + Bbar x: one add and one fma per state.
 // A wave whose channels have some A == 0 switches to the explicit form with the
-// Delta * B limit.
+// Delta * B limit.  With the Euler rule (Bbar = Delta B, the page-3 report's code,
+// section 4.2) the prologue stages Delta*x instead of x and the update is
+// h <- Abar h + (Delta x) B.
 //
 // Long sequences are split into segments (a two-level scan over the sequence):
 // an aggregate pass scans each segment from a zero state and records its end
@@ -110,7 +112,8 @@ __device__ __forceinline__ int64_t after(int64_t v, float dep) {
 
 // One workgroup: (batch row b, 64-channel tile, segment); NSPLIT waves x NPW states.
 // NFIX: N as a compile-time constant (0 = read it from the shape at run time).
-template <typename Tin, int NSPLIT, int NPW, bool AGG, bool PAIR, int NFIX>
+// EULER: Bbar = Delta B instead of the zero-order hold.
+template <typename Tin, int NSPLIT, int NPW, bool AGG, bool PAIR, int NFIX, bool EULER>
 __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
     const Tin* __restrict__ xg, const Tin* __restrict__ dtg, const Tin* __restrict__ zg,
     const Tin* __restrict__ Bg, const Tin* __restrict__ Cg, const float* __restrict__ Ag,
@@ -123,8 +126,8 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
   static_assert(T % NSPLIT == 0, "chunk must split evenly over waves");
   static_assert(NPW == 1 || NPW == 2, "one or two states per wave");
 
-  // Delta*log2(e) and x of each staged timestep, as two 32-bit arrays (32-bit LDS
-  // reads run at about twice the rate of 64-bit ones here).
+  // Delta*log2(e) and x (Delta*x for EULER) of each staged timestep, as two 32-bit
+  // arrays (32-bit LDS reads run at about twice the rate of 64-bit ones here).
   __shared__ float s_d2[2][T][kTile];
   __shared__ float s_xv[2][T][kTile];
   // States after each timestep, for the readout C.h done by the epilogue wave.
@@ -259,7 +262,7 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
       float d2 = softplus_log2e(fmaf(to_f32(rdt[i]), kLog2e, bias2));
       d2 = lv ? d2 : 0.f;  // a padded step is the identity: Delta = 0, x = 0
       s_d2[P][t][lane] = d2;
-      s_xv[P][t][lane] = xv;
+      s_xv[P][t][lane] = EULER ? (d2 * kLn2) * xv : xv;
       if constexpr (AGG) {
         const float yk = d2 - scomp;
         const float tk = ssum + yk;
@@ -278,7 +281,17 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
   auto run_steps = [&](auto pc, auto hc, const float2* vx, const float (*ea)[NPW]) {
     constexpr int P = decltype(pc)::value;
     constexpr int HH = decltype(hc)::value;
-    if (!zeroA) {
+    if constexpr (EULER) {
+      // vx[t].y holds Delta * x; phantom states are never read back.
+#pragma unroll
+      for (int t = HH * H; t < (HH + 1) * H; ++t) {
+#pragma unroll
+        for (int j = 0; j < NPW; ++j) {
+          h[j] = fmaf(ea[t][j], h[j], vx[t].y * bc[t].get(j, sel));
+          if constexpr (!AGG) s_h[P][n0 + j][t][lane] = h[j];
+        }
+      }
+    } else if (!zeroA) {
 #pragma unroll
       for (int t = HH * H; t < (HH + 1) * H; ++t) {
 #pragma unroll
@@ -470,29 +483,37 @@ int fwd_nsplit(int N) {
 
 namespace {
 
-template <typename Tin, int NS, bool AGG, bool PR, int NF>
+template <typename Tin, int NS, bool AGG, bool PR, int NF, bool EU>
 void launch_one(const FwdParams& p, dim3 grid, hipStream_t s) {
   FwdShape sh{p.batch, p.L, p.dim, p.seg_len, p.ndtiles, p.N, p.nseg};
-  hipLaunchKernelGGL((fwd_kernel<Tin, NS, 1, AGG, PR, NF>), grid, dim3(NS * 64), 0, s,
+  hipLaunchKernelGGL((fwd_kernel<Tin, NS, 1, AGG, PR, NF, EU>), grid, dim3(NS * 64), 0, s,
                      static_cast<const Tin*>(p.x), static_cast<const Tin*>(p.dt), static_cast<const Tin*>(p.z),
                      static_cast<const Tin*>(p.B), static_cast<const Tin*>(p.C), p.A, p.Dskip, p.bias, p.h_init,
                      static_cast<Tin*>(p.y), p.h_last, p.agg_h, p.agg_s, sh);
 }
 
-template <typename Tin, bool AGG, bool PR>
+template <typename Tin, bool AGG, bool PR, bool EU>
 void launch_by_n(const FwdParams& p, dim3 grid, hipStream_t s) {
   switch (fwd_nsplit(p.N)) {
-    case 1: launch_one<Tin, 1, AGG, PR, 0>(p, grid, s); break;
-    case 2: launch_one<Tin, 2, AGG, PR, 0>(p, grid, s); break;
-    case 4: launch_one<Tin, 4, AGG, PR, 0>(p, grid, s); break;
-    case 8: launch_one<Tin, 8, AGG, PR, 0>(p, grid, s); break;
+    case 1: launch_one<Tin, 1, AGG, PR, 0, EU>(p, grid, s); break;
+    case 2: launch_one<Tin, 2, AGG, PR, 0, EU>(p, grid, s); break;
+    case 4: launch_one<Tin, 4, AGG, PR, 0, EU>(p, grid, s); break;
+    case 8: launch_one<Tin, 8, AGG, PR, 0, EU>(p, grid, s); break;
     default:
       if (p.N == 16)
-        launch_one<Tin, 16, AGG, PR, 16>(p, grid, s);
+        launch_one<Tin, 16, AGG, PR, 16, EU>(p, grid, s);
       else
-        launch_one<Tin, 16, AGG, PR, 0>(p, grid, s);
+        launch_one<Tin, 16, AGG, PR, 0, EU>(p, grid, s);
       break;
   }
+}
+
+template <typename Tin, bool AGG, bool PR>
+void launch_by_rule(const FwdParams& p, dim3 grid, hipStream_t s) {
+  if (p.euler)
+    launch_by_n<Tin, AGG, PR, true>(p, grid, s);
+  else
+    launch_by_n<Tin, AGG, PR, false>(p, grid, s);
 }
 
 template <bool AGG>
@@ -503,11 +524,11 @@ hipError_t launch_fwd_impl(const FwdParams& p, bool bf16, hipStream_t s) {
   const bool pair = bf16 && (p.N % 2 == 0) && ((reinterpret_cast<uintptr_t>(p.B) & 3) == 0) &&
                     ((reinterpret_cast<uintptr_t>(p.C) & 3) == 0);
   if (!bf16)
-    launch_by_n<float, AGG, false>(p, grid, s);
+    launch_by_rule<float, AGG, false>(p, grid, s);
   else if (pair)
-    launch_by_n<bf16_t, AGG, true>(p, grid, s);
+    launch_by_rule<bf16_t, AGG, true>(p, grid, s);
   else
-    launch_by_n<bf16_t, AGG, false>(p, grid, s);
+    launch_by_rule<bf16_t, AGG, false>(p, grid, s);
   return hipGetLastError();
 }
 

@@ -28,6 +28,7 @@ struct FwdParams {
   int64_t ndtiles;        // ceil(dim / kTile)
   int N;
   int nseg;
+  bool euler;             // Bbar = Delta * B instead of the zero-order hold
 };
 
 // Sizes passed by value to the forward kernels (pointers go as separate
@@ -50,6 +51,7 @@ struct StepParams {
   void* y;
   int64_t batch, dim;
   int N;
+  bool euler;             // Bbar = Delta * B instead of the zero-order hold
 };
 
 // Waves per workgroup of the forward kernels for a given N (each wave owns one state).

@@ -4,6 +4,7 @@
 // discretization as in the velog.io review, "Discretization"):
 //   Delta = softplus(dt + bias), Abar = exp(Delta A), Bbar = (Abar - 1)/A * B
 //   (Delta * B when A == 0), h <- Abar h + Bbar x (in place), y = (C . h + D x) silu(z).
+// With the Euler rule (page-3 report, section 4.2) Bbar = Delta * B.
 //
 // The step is bound by reading and writing the fp32 state [batch, dim, N].  Each
 // lane holds 8 (or 4) consecutive states of one (b, d) row, read and written with
@@ -34,8 +35,8 @@ __device__ __forceinline__ void load4(const Tin* __restrict__ p, int n0, int N, 
 
 // SPL states per lane (4 or 8), LPR = ceil(N / SPL) lanes per (b, d) row.  VEC: N is a
 // multiple of 4 and state, A, B, C allow 16-byte (8-byte for bf16 B/C) accesses.
-// NFIX: N as a compile-time constant (0 = run time).
-template <typename Tin, int SPL, int LPR, bool VEC, int NFIX>
+// NFIX: N as a compile-time constant (0 = run time).  EULER: Bbar = Delta B.
+template <typename Tin, int SPL, int LPR, bool VEC, int NFIX, bool EULER>
 __global__ __launch_bounds__(256) void step_kernel(float* __restrict__ S, const Tin* __restrict__ X,
                                                    const Tin* __restrict__ DT, const Tin* __restrict__ Z,
                                                    const Tin* __restrict__ Bp, const Tin* __restrict__ Cp,
@@ -80,7 +81,7 @@ __global__ __launch_bounds__(256) void step_kernel(float* __restrict__ S, const 
     for (int j = 0; j < SPL; ++j) {
       const float e = hw_exp2(d2 * a[j]);
       // (Abar - 1) / A, or Delta in the limit A = 0
-      const float g = (a[j] != 0.f) ? (e - 1.f) * hw_rcp(a[j]) : dl;
+      const float g = (EULER || a[j] == 0.f) ? dl : (e - 1.f) * hw_rcp(a[j]);
       h[j] = fmaf(e, h[j], g * bv[j] * xv);
       yp = fmaf(cv[j], h[j], yp);
     }
@@ -106,28 +107,28 @@ __global__ __launch_bounds__(256) void step_kernel(float* __restrict__ S, const 
 
 namespace {
 
-template <typename Tin, int SPL, int LPR, bool VEC, int NF>
+template <typename Tin, int SPL, int LPR, bool VEC, int NF, bool EU>
 void launch_step_one(const StepParams& p, hipStream_t s) {
   const int64_t rows = p.batch * p.dim;
   const int64_t threads = rows * LPR;
-  hipLaunchKernelGGL((step_kernel<Tin, SPL, LPR, VEC, NF>), dim3(static_cast<unsigned>((threads + 255) / 256)),
+  hipLaunchKernelGGL((step_kernel<Tin, SPL, LPR, VEC, NF, EU>), dim3(static_cast<unsigned>((threads + 255) / 256)),
                      dim3(256), 0, s, p.state, static_cast<const Tin*>(p.x), static_cast<const Tin*>(p.dt),
                      static_cast<const Tin*>(p.z), static_cast<const Tin*>(p.B), static_cast<const Tin*>(p.C), p.A,
                      p.Dskip, p.bias, static_cast<Tin*>(p.y), rows, p.dim, p.N);
 }
 
-template <typename Tin>
+template <typename Tin, bool EU>
 void launch_step_t(const StepParams& p, bool vec, hipStream_t s) {
   if (p.N == 16 && vec) {
-    launch_step_one<Tin, 8, 2, true, 16>(p, s);  // 8 states per lane
+    launch_step_one<Tin, 8, 2, true, 16, EU>(p, s);  // 8 states per lane
   } else if (vec) {
-    if (p.N <= 4) launch_step_one<Tin, 4, 1, true, 0>(p, s);
-    else if (p.N <= 8) launch_step_one<Tin, 8, 1, true, 0>(p, s);
-    else launch_step_one<Tin, 8, 2, true, 0>(p, s);
+    if (p.N <= 4) launch_step_one<Tin, 4, 1, true, 0, EU>(p, s);
+    else if (p.N <= 8) launch_step_one<Tin, 8, 1, true, 0, EU>(p, s);
+    else launch_step_one<Tin, 8, 2, true, 0, EU>(p, s);
   } else {
-    if (p.N <= 4) launch_step_one<Tin, 4, 1, false, 0>(p, s);
-    else if (p.N <= 8) launch_step_one<Tin, 8, 1, false, 0>(p, s);
-    else launch_step_one<Tin, 8, 2, false, 0>(p, s);
+    if (p.N <= 4) launch_step_one<Tin, 4, 1, false, 0, EU>(p, s);
+    else if (p.N <= 8) launch_step_one<Tin, 8, 1, false, 0, EU>(p, s);
+    else launch_step_one<Tin, 8, 2, false, 0, EU>(p, s);
   }
 }
 
@@ -141,9 +142,9 @@ hipError_t launch_step(const StepParams& p, bool bf16, hipStream_t s) {
                    ((reinterpret_cast<uintptr_t>(p.A) & 15) == 0) && ((reinterpret_cast<uintptr_t>(p.B) & bcal) == 0) &&
                    ((reinterpret_cast<uintptr_t>(p.C) & bcal) == 0);
   if (bf16)
-    launch_step_t<bf16_t>(p, vec, s);
+    p.euler ? launch_step_t<bf16_t, true>(p, vec, s) : launch_step_t<bf16_t, false>(p, vec, s);
   else
-    launch_step_t<float>(p, vec, s);
+    p.euler ? launch_step_t<float, true>(p, vec, s) : launch_step_t<float, false>(p, vec, s);
   return hipGetLastError();
 }
 

@@ -17,10 +17,10 @@ def lib():
         from selective_state_space_45_amd import build as b
         b.build()
     lb = ctypes.CDLL(LIB)
-    P, I64, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
-    lb.sscan_fwd.argtypes = [I64, I64, I64, I64, ctypes.c_int] + [P] * 11 + [P, SZ, P]
-    lb.sscan_fwd_segmented.argtypes = [I64, I64, I64, I64, ctypes.c_int] + [P] * 11 + [P, SZ, I64, P]
-    lb.sscan_step.argtypes = [I64, I64, I64, ctypes.c_int] + [P] * 11
+    P, I64, SZ, U32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_uint
+    lb.sscan_fwd.argtypes = [I64, I64, I64, I64, ctypes.c_int, U32] + [P] * 11 + [P, SZ, P]
+    lb.sscan_fwd_segmented.argtypes = [I64, I64, I64, I64, ctypes.c_int, U32] + [P] * 11 + [P, SZ, I64, P]
+    lb.sscan_step.argtypes = [I64, I64, I64, ctypes.c_int, U32] + [P] * 11
     lb.sscan_last_error.restype = ctypes.c_char_p
     lb.sscan_fwd_workspace_size.argtypes = [I64, I64, I64, I64, ctypes.c_int]
     lb.sscan_fwd_workspace_size.restype = SZ
@@ -55,10 +55,10 @@ FAKE = ctypes.c_void_p(0x10000)      # never dereferenced: every call below fail
 FAKE2 = ctypes.c_void_p(0x20000)
 
 
-def fwd(lib, batch=2, L=8, dim=4, N=4, dtype=0, x=FAKE, dt=FAKE2, A=ctypes.c_void_p(0x30000),
+def fwd(lib, batch=2, L=8, dim=4, N=4, dtype=0, flags=0, x=FAKE, dt=FAKE2, A=ctypes.c_void_p(0x30000),
         B=ctypes.c_void_p(0x40000), C=ctypes.c_void_p(0x50000), D=None, z=None, bias=None, h0=None,
         y=ctypes.c_void_p(0x60000), hl=None):
-    return lib.sscan_fwd(batch, L, dim, N, dtype, x, dt, A, B, C, D, z, bias, h0, y, hl, None, 0, None)
+    return lib.sscan_fwd(batch, L, dim, N, dtype, flags, x, dt, A, B, C, D, z, bias, h0, y, hl, None, 0, None)
 
 
 @pytest.mark.parametrize("N", [0, 17, -1])
@@ -69,6 +69,17 @@ def test_dstate_outside_range_is_unsupported(lib, N):
 
 def test_unknown_dtype_is_unsupported(lib):
     assert fwd(lib, dtype=7) == 2
+
+
+@pytest.mark.parametrize("flags", [2, 0x80000000, 3])
+def test_unknown_flag_bits_are_unsupported(lib, flags):
+    assert fwd(lib, flags=flags) == 2
+    assert b"flag" in lib.sscan_last_error()
+
+
+def test_header_defines_euler_flag():
+    text = open(HEADER).read()
+    assert re.search(r"#define SSCAN_FLAG_EULER 1u", text)
 
 
 @pytest.mark.parametrize("kw", [dict(batch=-1), dict(L=-3), dict(dim=-2)])
@@ -103,14 +114,16 @@ def test_empty_problems_are_noops(lib):
 def test_step_validation(lib):
     P = ctypes.c_void_p
     args = [P(0x10000), P(0x20000), P(0x30000), P(0x40000), P(0x50000), P(0x60000), None, None, None, P(0x70000), None]
-    assert lib.sscan_step(4, 8, 17, 0, *args) == 2
-    assert lib.sscan_step(4, 8, 4, 0, None, *args[1:]) == 1
-    assert lib.sscan_step(0, 8, 4, 0, *args) == 0
+    assert lib.sscan_step(4, 8, 17, 0, 0, *args) == 2
+    assert lib.sscan_step(4, 8, 4, 0, 0, None, *args[1:]) == 1
+    assert lib.sscan_step(4, 8, 4, 0, 4, *args) == 2     # unknown flag bit
+    assert lib.sscan_step(0, 8, 4, 0, 0, *args) == 0
+    assert lib.sscan_step(0, 8, 4, 0, 1, *args) == 0     # Euler flag accepted
 
 
 def test_segmented_rejects_negative_segment_count(lib):
     P = ctypes.c_void_p
-    rc = lib.sscan_fwd_segmented(2, 8, 4, 4, 0, FAKE, FAKE2, P(0x30000), P(0x40000), P(0x50000), None, None, None,
+    rc = lib.sscan_fwd_segmented(2, 8, 4, 4, 0, 0, FAKE, FAKE2, P(0x30000), P(0x40000), P(0x50000), None, None, None,
                                  None, P(0x60000), None, None, 0, -2, None)
     assert rc == 1
 

@@ -58,7 +58,7 @@ def host(t):
     return t.float().cpu().numpy()
 
 
-def run_gpu(ss, w, h0=None, num_segments=None, want_state=True, poison=True):
+def run_gpu(ss, w, h0=None, num_segments=None, want_state=True, poison=True, euler=False):
     import torch
     x, dt, z = tdev(w.x, w.dtype), tdev(w.dt, w.dtype), tdev(w.z, w.dtype)
     B, C = tdev(w.B, w.dtype), tdev(w.C, w.dtype)
@@ -70,13 +70,13 @@ def run_gpu(ss, w, h0=None, num_segments=None, want_state=True, poison=True):
         if st is not None:
             st.fill_(float("nan"))
     ss.sscan_fwd(x, dt, A, B, C, D=D, z=z, delta_bias=bias, initial_state=f32dev(h0), out=y,
-                 last_state=st, num_segments=num_segments)
+                 last_state=st, num_segments=num_segments, euler=euler)
     torch.cuda.synchronize()
     return host(y), (host(st) if st is not None else None)
 
 
-def run_oracle(orc, w, h0=None):
-    return orc.sscan_fwd(w.x, w.dt, w.A, w.B, w.C, D=w.D, z=w.z, dt_bias=w.dt_bias, h0=h0)
+def run_oracle(orc, w, h0=None, euler=False):
+    return orc.sscan_fwd(w.x, w.dt, w.A, w.B, w.C, D=w.D, z=w.z, dt_bias=w.dt_bias, h0=h0, euler=euler)
 
 
 def assert_close(got, ref, tau, what):
@@ -90,11 +90,11 @@ def assert_close(got, ref, tau, what):
     return float(err.max()) if err.size else 0.0
 
 
-def check_workload(ss, orc, w, h0=None, num_segments=None, label=""):
+def check_workload(ss, orc, w, h0=None, num_segments=None, label="", euler=False):
     note(f"[case] {label or w.name}: B={w.batch} L={w.seqlen} D={w.dim} N={w.dstate} {w.dtype} "
-         f"seed={w.meta.get('seed')} segments={num_segments}")
-    y, st = run_gpu(ss, w, h0=h0, num_segments=num_segments)
-    yr, sr = run_oracle(orc, w, h0=h0)
+         f"seed={w.meta.get('seed')} segments={num_segments} euler={euler}")
+    y, st = run_gpu(ss, w, h0=h0, num_segments=num_segments, euler=euler)
+    yr, sr = run_oracle(orc, w, h0=h0, euler=euler)
     tau = TAU[w.dtype]
     ey = assert_close(y, yr, tau, "y")
     es = assert_close(st, sr, tau, "last_state")

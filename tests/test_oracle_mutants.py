@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 
 import oracle
+import test_oracle_euler_pins as euler_pins
 import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "sscan_oracle.c")
@@ -30,12 +31,15 @@ MUTANTS = [
     ("delta_is_raw_dt", "const double delta = softplus(dt[i] + bd);", "const double delta = dt[i] + bd;"),
     ("A_index_transposed_square", "const double an = A[d * N + n];", "const double an = A[(n % Dm) * N + (d % N)];"),
     ("last_state_stale", "h_last[(b * Dm + d) * N + n] = h[n];", "h_last[(b * Dm + d) * N + n] = 0.0;"),
+    ("euler_flag_ignored", "(an != 0.0 && !euler)", "(an != 0.0)"),
+    ("euler_flag_inverted", "(an != 0.0 && !euler)", "(an != 0.0 && euler)"),
 ]
 
 
 def _pin_functions():
     out = []
-    for name, fn in inspect.getmembers(pins, inspect.isfunction):
+    members = inspect.getmembers(pins, inspect.isfunction) + inspect.getmembers(euler_pins, inspect.isfunction)
+    for name, fn in members:
         if not name.startswith("test_"):
             continue
         params = list(inspect.signature(fn).parameters)
