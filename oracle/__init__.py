@@ -23,6 +23,9 @@ What it computes, and the passages it follows (the reference pages):
 * Recurrent step on a carried (B, D, N) state: page-3 report section 6 (ssm_step).
 * ``euler=True``: Bbar = Delta B, the first-order rule of the page-3 report's code
   (section 4.2, ``deltaB = delta * B``).
+* ``sscan_bwd``: gradients of a scalar loss with respect to every input, by the
+  chain rule through the definition above, run backwards in time (the reverse
+  recurrence that the page-3 report's ``pscan_rev`` serves, section 4.1).
 
 Parity status: every function here is pinned by the ``-m "not gpu"`` tests in
 ``tests/test_oracle_pins.py`` (closed forms, a hand-derived worked example,
@@ -83,6 +86,8 @@ class Oracle:
         lib.oracle_sscan_fwd.restype = ctypes.c_int
         lib.oracle_sscan_step.argtypes = [I64, I64, I64, ctypes.c_int] + [P] * 10 + [ctypes.c_int]
         lib.oracle_sscan_step.restype = ctypes.c_int
+        lib.oracle_sscan_bwd.argtypes = [I64, I64, I64, I64, ctypes.c_int] + [P] * 20 + [ctypes.c_int]
+        lib.oracle_sscan_bwd.restype = ctypes.c_int
         lib.oracle_nthreads_default.argtypes = []
         lib.oracle_nthreads_default.restype = ctypes.c_int
         self.lib = lib
@@ -149,6 +154,45 @@ class Oracle:
         return y
 
 
+    def sscan_bwd(self, x, dt, A, B, C, dy, D=None, z=None, dt_bias=None, h0=None, dlast_state=None,
+                  euler: bool = False, nthreads: int = 0) -> dict:
+        """fp64 backward pass.  Same inputs as ``sscan_fwd`` plus dy [batch, seqlen, dim]
+        (dLoss/dy) and optionally dlast_state [batch, dim, dstate] (dLoss/d last state).
+        Returns a dict of gradients: dx, ddt, dz (if z), dA, dB, dC, dD (if D),
+        ddt_bias (always; the gradient at bias = 0 when absent), dh0."""
+        x = _f64(x, name="x")
+        if x.ndim != 3:
+            raise ValueError("x must be [batch, seqlen, dim]")
+        Bt, L, Dm = x.shape
+        A = _f64(A, name="A")
+        if A.ndim != 2 or A.shape[0] != Dm:
+            raise ValueError("A must be [dim, dstate]")
+        N = A.shape[1]
+        dt = _f64(dt, (Bt, L, Dm), "dt")
+        B = _f64(B, (Bt, L, N), "B")
+        C = _f64(C, (Bt, L, N), "C")
+        dy = _f64(dy, (Bt, L, Dm), "dy")
+        D = _f64(D, (Dm,), "D")
+        z = _f64(z, (Bt, L, Dm), "z")
+        dt_bias = _f64(dt_bias, (Dm,), "dt_bias")
+        h0 = _f64(h0, (Bt, Dm, N), "h0")
+        dhl = _f64(dlast_state, (Bt, Dm, N), "dlast_state")
+        out = {"dx": np.empty((Bt, L, Dm)), "ddt": np.empty((Bt, L, Dm)), "dA": np.empty((Dm, N)),
+               "dB": np.empty((Bt, L, N)), "dC": np.empty((Bt, L, N)),
+               "dD": np.empty(Dm) if D is not None else None,
+               "dz": np.empty((Bt, L, Dm)) if z is not None else None,
+               "ddt_bias": np.empty(Dm), "dh0": np.empty((Bt, Dm, N))}
+        used = self.lib.oracle_sscan_bwd(Bt, L, Dm, N, int(bool(euler)), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+                                         _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias), _ptr(h0), _ptr(dy),
+                                         _ptr(dhl), _ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["dA"]),
+                                         _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dz"]),
+                                         _ptr(out["ddt_bias"]), _ptr(out["dh0"]), int(nthreads))
+        if used < 0:
+            raise ValueError("oracle_sscan_bwd rejected its arguments")
+        self.last_threads_used = used
+        return out
+
+
 _default: Optional[Oracle] = None
 
 
@@ -173,6 +217,11 @@ def sscan_fwd(*args, **kwargs):
 def sscan_step(*args, **kwargs):
     """fp64 single-token step (see ``Oracle.sscan_step``)."""
     return _load().sscan_step(*args, **kwargs)
+
+
+def sscan_bwd(*args, **kwargs):
+    """fp64 backward pass (see ``Oracle.sscan_bwd``)."""
+    return _load().sscan_bwd(*args, **kwargs)
 
 
 def last_threads_used() -> int:

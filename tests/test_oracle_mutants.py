@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 
 import oracle
+import test_oracle_bwd_pins as bwd_pins
 import test_oracle_euler_pins as euler_pins
 import test_oracle_pins as pins
 
@@ -33,12 +34,23 @@ MUTANTS = [
     ("last_state_stale", "h_last[(b * Dm + d) * N + n] = h[n];", "h_last[(b * Dm + d) * N + n] = 0.0;"),
     ("euler_flag_ignored", "(an != 0.0 && !euler)", "(an != 0.0)"),
     ("euler_flag_inverted", "(an != 0.0 && !euler)", "(an != 0.0 && euler)"),
+    # backward pass
+    ("bwd_gradient_not_decayed", "gh[n] = abar * g;", "gh[n] = g;"),
+    ("bwd_dB_missing_x", "dBm[r + n] += g * phi * xv;", "dBm[r + n] += g * phi;"),
+    ("bwd_dC_previous_state", "dCm[r + n] += gyo * hs[(l + 1) * N + n];", "dCm[r + n] += gyo * hs[l * N + n];"),
+    ("bwd_ddt_no_sigmoid", "const double gdt = gdelta * sigmoid(v);", "const double gdt = gdelta;"),
+    ("bwd_dA_missing_input_term", "+ dphi_dA * Bm[r + n] * xv);", ");"),
+    ("bwd_dz_sign", "(1.0 + zz * (1.0 - sg))", "(1.0 - zz * (1.0 - sg))"),
+    ("bwd_series_factorial", "fact *= (double)(k + 3);", "fact *= (double)(k + 2);"),
+    ("bwd_dx_missing_skip", "double gx = Dskip ? gyo * Dskip[d] : 0.0;", "double gx = 0.0;"),
+    ("bwd_ddelta_decay_term_sign", "gdelta += g * (an * abar * hprev", "gdelta += g * (-an * abar * hprev"),
 ]
 
 
 def _pin_functions():
     out = []
-    members = inspect.getmembers(pins, inspect.isfunction) + inspect.getmembers(euler_pins, inspect.isfunction)
+    members = (inspect.getmembers(pins, inspect.isfunction) + inspect.getmembers(euler_pins, inspect.isfunction)
+               + inspect.getmembers(bwd_pins, inspect.isfunction))
     for name, fn in members:
         if not name.startswith("test_"):
             continue
