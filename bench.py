@@ -7,7 +7,7 @@ bf16 x/delta/z/B/C/y, fp32 A/D/bias/state.  Inputs are resident in HBM before th
 timed region.  One JSON line is printed.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
-                    [--no-euler] [--copy-calibration]
+                    [--no-euler] [--no-bwd] [--copy-calibration]
     python bench.py --summarize-counters FETCH_CSV WRITE_CSV   (CPU only)
 
 --copy-calibration also runs a plain 512 MiB -> 512 MiB elementwise copy (three
@@ -119,6 +119,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline leg")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step leg")
     ap.add_argument("--no-euler", action="store_true", help="skip the Euler-rule leg")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward-pass leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 512 MiB elementwise copy (counter calibration)")
     ap.add_argument("--decode-steps", type=int, default=100)
@@ -195,6 +196,28 @@ def main():
         euler = {"op": "sscan_fwd, Euler rule (flag SSCAN_FLAG_EULER)", "kernel_ms": round(eu_ms, 5),
                  "gbs": round(nbytes / (eu_ms * 1e-3) / 1e9, 2),
                  "hbm_frac_of_peak": round(nbytes / (eu_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+    # backward pass (sscan_bwd: checkpoint pass, reverse pass, reductions) on the same
+    # workload, reported alongside
+    bwd = None
+    if not args.no_bwd:
+        gy = torch.randn_like(x)
+        bwd_ws = torch.empty(ss.bwd_workspace_size(w.batch, w.seqlen, w.dim, w.dstate, torch.bfloat16),
+                             dtype=torch.uint8, device=dev)
+        grads = {}
+
+        def step_bwd():
+            ss.sscan_bwd(x, dt, A, B, C, gy, D=D, z=z, delta_bias=bias, workspace=bwd_ws, out=grads)
+
+        for _ in range(3):
+            step_bwd()
+        torch.cuda.synchronize()
+        bw_ms = timed_launches(step_bwd, max(5, args.steps // 5))
+        # inputs x, dt, z, dy, B, C (+A, D, bias) read once; dx, ddt, dz, dB, dC (+dA, dD, dbias) written once
+        bw_bytes = W.bwd_algorithmic_bytes(w.batch, w.seqlen, w.dim, w.dstate, "bf16")
+        bwd = {"op": "sscan_bwd (checkpoint pass + reverse pass + reductions)", "ms": round(bw_ms, 5),
+               "algorithmic_bytes": bw_bytes, "gbs": round(bw_bytes / (bw_ms * 1e-3) / 1e9, 2),
+               "tokens_channels_per_s": round(tokch / (bw_ms * 1e-3), 1)}
 
     # decode step (sscan_step) on the decode workload, reported alongside.  The steps
     # are captured in a HIP graph and replayed, so host-side launch overhead is not
@@ -283,6 +306,7 @@ def main():
                      "kernel_ms": round(kern_ms, 5), "kernel_gbs": round(kern_gbs, 2),
                      "algorithmic_bytes": nbytes, "algorithmic_ops": ops},
         "euler": euler,
+        "bwd": bwd,
         "decode": decode,
         "cpu_baseline": cpu,
     }

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define SSCAN_VERSION 200
+#define SSCAN_VERSION 300
 #define SSCAN_MAX_DSTATE 16
 
 /*
@@ -144,6 +144,61 @@ int sscan_step(int64_t batch, int64_t dim, int64_t dstate, int dtype, unsigned i
                float* state, const void* x, const void* delta, const float* A,
                const void* B, const void* C, const float* D, const void* z,
                const float* delta_bias, void* y, void* stream);
+
+/*
+ * Workspace bytes sscan_bwd needs for a shape (0 for an empty problem).  The
+ * backward pass cannot run without it: it holds the state checkpoints (one per
+ * 16 timesteps), per-channel-tile partial sums of dB and dC, per-batch-row
+ * partial sums of dA, dD and ddelta_bias, and the sequence-split buffers of the
+ * checkpoint pass.  Contents are scratch: nothing is kept between calls.
+ */
+size_t sscan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                int dtype);
+
+/*
+ * Backward pass of sscan_fwd: gradients of a scalar loss with respect to every
+ * input, given dy = dLoss/dy and, optionally, dlast_state = dLoss/d(last_state).
+ *
+ * The gradients are the chain rule through the forward definition at the top of
+ * this header, run backwards in time: the reverse recurrence
+ *   g_l = gyo_l C_l + Abar_{l+1} g_{l+1},   gyo_l = dy_l silu(z_l)   (elementwise in N)
+ * that the page-3 report's PScan.backward computes with its reverse scan
+ * pscan_rev (Mamba_Model_Report.md, section 4.1), with the forward states
+ * recomputed rather than stored (the recomputation that the lengnian.github.io
+ * notes, "Part3: Mamba - A Selective SSM", list in the hardware-aware algorithm).
+ * Gradients then follow per step (phi = Bbar / B):
+ *   dx = gyo D + sum_n g phi B        dB = sum_d g phi x        dC = sum_d gyo h
+ *   dz = dy (C.h + D x) silu'(z)      dD = sum_{b,l} gyo x
+ *   ddelta = sigmoid(delta + delta_bias) sum_n g (A Abar h_{l-1} + dphi/dDelta B x)
+ *   dA = sum_{b,l} g (Delta Abar h_{l-1} + dphi/dA B x),  ddelta_bias = sum_{b,l} ddelta
+ *   dinitial_state = Abar_0 g_0
+ * (zero-order hold: phi = (Abar - 1)/A, dphi/dDelta = Abar, dphi/dA = (Delta Abar - phi)/A,
+ * Delta^2/2 at A = 0; SSCAN_FLAG_EULER: phi = Delta, dphi/dDelta = 1, dphi/dA = 0).
+ *
+ *   inputs  : as sscan_fwd (x, delta, A, B, C, D, z, delta_bias, initial_state, flags)
+ *   dy      : [batch, seqlen, dim]    (dtype)
+ *   dlast_state : [batch, dim, dstate] (float32), NULL = zero
+ *   dx, ddelta, dz : [batch, seqlen, dim]    (dtype)
+ *   dB, dC         : [batch, seqlen, dstate] (dtype)
+ *   dA             : [dim, dstate]           (float32)
+ *   dD, ddelta_bias: [dim]                   (float32)
+ *   dinitial_state : [batch, dim, dstate]    (float32)
+ *
+ * Required: x, delta, A, B, C, dy, dx, ddelta, dA, dB, dC and the workspace
+ * (at least sscan_bwd_workspace_size bytes, 256-byte aligned).  dz is required
+ * exactly when z is given; dD may be given only with D; ddelta_bias and
+ * dinitial_state are optional whether or not delta_bias / initial_state are
+ * (they are then the gradients at a zero bias / zero initial state).
+ * Outputs must not overlap inputs, each other or the workspace.  Reductions run
+ * in a fixed order: results are bitwise reproducible.
+ */
+int sscan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+              unsigned int flags, const void* x, const void* delta, const float* A, const void* B,
+              const void* C, const float* D, const void* z, const float* delta_bias,
+              const float* initial_state, const void* dy, const float* dlast_state, void* dx,
+              void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz,
+              float* ddelta_bias, float* dinitial_state, void* workspace, size_t workspace_bytes,
+              void* stream);
 
 #ifdef __cplusplus
 }

@@ -154,8 +154,7 @@ int oracle_sscan_step(int64_t batch, int64_t dim, int64_t dstate, int euler, dou
  * state) [batch][dim][dstate], it returns the gradients with respect to every
  * input.  This is the chain rule applied to the forward definition above, run
  * backwards in time (the reverse recurrence the page-3 report's pscan_rev serves,
- * section 4.1; recomputing intermediates instead of storing them, as the
- * lengnian.github.io notes describe for the hardware-aware scan):
+ * section 4.1):
  *
  *   s(z)    = silu(z), s'(z) = sigmoid(z) (1 + z (1 - sigmoid(z)))
  *   yo_l    = sum_n C[l,n] h_l[n] + D x_l                 (output before the gate)

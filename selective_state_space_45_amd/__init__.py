@@ -39,6 +39,10 @@ _lib.sscan_fwd_segmented.argtypes = [_I64, _I64, _I64, _I64, ctypes.c_int, _U32]
 _lib.sscan_fwd_segmented.restype = ctypes.c_int
 _lib.sscan_step.argtypes = [_I64, _I64, _I64, ctypes.c_int, _U32] + [_P] * 11
 _lib.sscan_step.restype = ctypes.c_int
+_lib.sscan_bwd_workspace_size.argtypes = [_I64, _I64, _I64, _I64, ctypes.c_int]
+_lib.sscan_bwd_workspace_size.restype = _SZ
+_lib.sscan_bwd.argtypes = [_I64, _I64, _I64, _I64, ctypes.c_int, _U32] + [_P] * 21 + [_SZ, _P]
+_lib.sscan_bwd.restype = ctypes.c_int
 
 SSCAN_F32, SSCAN_BF16 = 0, 1
 SSCAN_FLAG_EULER = 1
@@ -179,3 +183,67 @@ def sscan_step(state: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, A: tor
     _check(_lib.sscan_step(batch, dim, dstate, _DTYPES[x.dtype], SSCAN_FLAG_EULER if euler else 0, _ptr(state), _ptr(x), _ptr(delta), _ptr(A),
                            _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(y), _stream(x.device)))
     return y
+
+
+def bwd_workspace_size(batch: int, seqlen: int, dim: int, dstate: int, dtype=torch.bfloat16) -> int:
+    return int(_lib.sscan_bwd_workspace_size(batch, seqlen, dim, dstate, _DTYPES[dtype]))
+
+
+def sscan_bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+              dy: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+              delta_bias: Optional[torch.Tensor] = None, initial_state: Optional[torch.Tensor] = None,
+              dlast_state: Optional[torch.Tensor] = None, euler: bool = False,
+              want_ddelta_bias: bool = True, want_dinitial_state: bool = True,
+              workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None) -> dict:
+    """Backward pass of ``sscan_fwd``: gradients of a scalar loss given dy = dLoss/dy
+    (same shape and dtype as x) and optionally dlast_state = dLoss/d(last state).
+    Returns a dict with dx, ddelta, dA, dB, dC and, as applicable, dD, dz,
+    ddelta_bias, dinitial_state (``out`` may supply preallocated tensors by name)."""
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, seqlen, dim]")
+    batch, seqlen, dim = x.shape
+    if x.dtype not in _DTYPES:
+        raise ValueError("x must be float32 or bfloat16")
+    dstate = A.shape[1] if A.dim() == 2 else -1
+    _dev(x, "x")
+    _dev(delta, "delta", x.dtype, x.shape)
+    _dev(dy, "dy", x.dtype, x.shape)
+    _dev(A, "A", torch.float32, (dim, dstate))
+    _dev(B, "B", x.dtype, (batch, seqlen, dstate))
+    _dev(C, "C", x.dtype, (batch, seqlen, dstate))
+    for t, name, shape in ((D, "D", (dim,)), (delta_bias, "delta_bias", (dim,)),
+                           (initial_state, "initial_state", (batch, dim, dstate)),
+                           (dlast_state, "dlast_state", (batch, dim, dstate))):
+        if t is not None:
+            _dev(t, name, torch.float32, shape)
+    if z is not None:
+        _dev(z, "z", x.dtype, x.shape)
+    out = dict(out or {})
+    dev = x.device
+
+    def get(name, shape, dtype):
+        t = out.get(name)
+        if t is None:
+            t = torch.empty(shape, dtype=dtype, device=dev)
+            out[name] = t
+        return _dev(t, name, dtype, shape)
+
+    dx = get("dx", x.shape, x.dtype)
+    ddelta = get("ddelta", x.shape, x.dtype)
+    dA = get("dA", (dim, dstate), torch.float32)
+    dB = get("dB", (batch, seqlen, dstate), x.dtype)
+    dC = get("dC", (batch, seqlen, dstate), x.dtype)
+    dD = get("dD", (dim,), torch.float32) if D is not None else None
+    dz = get("dz", x.shape, x.dtype) if z is not None else None
+    dbias = get("ddelta_bias", (dim,), torch.float32) if want_ddelta_bias else None
+    dh0 = get("dinitial_state", (batch, dim, dstate), torch.float32) if want_dinitial_state else None
+    need = bwd_workspace_size(batch, seqlen, dim, dstate, x.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    wbytes = workspace.numel() * workspace.element_size()
+    flags = SSCAN_FLAG_EULER if euler else 0
+    _check(_lib.sscan_bwd(batch, seqlen, dim, dstate, _DTYPES[x.dtype], flags, _ptr(x), _ptr(delta), _ptr(A),
+                          _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(initial_state), _ptr(dy),
+                          _ptr(dlast_state), _ptr(dx), _ptr(ddelta), _ptr(dA), _ptr(dB), _ptr(dC), _ptr(dD),
+                          _ptr(dz), _ptr(dbias), _ptr(dh0), _ptr(workspace), wbytes, _stream(dev)))
+    return out

@@ -202,6 +202,153 @@ int fwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dty
   return ok();
 }
 
+
+// ---------------------------------------------------------------------------
+// Backward pass: workspace layout and host checks.
+// ---------------------------------------------------------------------------
+size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
+
+struct BwdLayout {
+  size_t ckpt, gB, gC, gA, gD, gb, seg, total;
+  int nseg;
+  int64_t seg_len;
+};
+
+BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t N) {
+  BwdLayout lo{};
+  const int64_t nblk = (seqlen + sscan::kBwdBlock - 1) / sscan::kBwdBlock;
+  const int64_t ndt = (dim + sscan::kTile - 1) / sscan::kTile;
+  size_t off = 0;
+  lo.ckpt = off; off += round256(static_cast<size_t>(batch) * nblk * N * dim * 4);
+  lo.gB = off;   off += round256(static_cast<size_t>(ndt) * batch * N * seqlen * 4);
+  lo.gC = off;   off += round256(static_cast<size_t>(ndt) * batch * N * seqlen * 4);
+  lo.gA = off;   off += round256(static_cast<size_t>(batch) * N * dim * 4);
+  lo.gD = off;   off += round256(static_cast<size_t>(batch) * dim * 4);
+  lo.gb = off;   off += round256(static_cast<size_t>(batch) * dim * 4);
+  const SegPlan pl = plan_segments(batch, seqlen, dim, N, 0, ~size_t(0), true);
+  lo.nseg = pl.nseg;
+  lo.seg_len = pl.seg_len;
+  lo.seg = off;  off += round256(seg_workspace_bytes(batch, dim, N, pl.nseg));
+  lo.total = off;
+  return lo;
+}
+
+int bwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype, unsigned flags, const void* x,
+             const void* delta, const float* A, const void* B, const void* C, const float* D, const void* z,
+             const float* delta_bias, const float* initial_state, const void* dy, const float* dlast_state,
+             void* dx, void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz, float* ddelta_bias,
+             float* dinitial_state, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_common(batch, dim, dstate, dtype, flags);
+  if (rc) return rc;
+  if (seqlen < 0) return fail(SSCAN_ERR_INVALID_ARG, "negative seqlen %lld", (long long)seqlen);
+  const int64_t max_elems = (int64_t(1) << 62) / 8;
+  if (batch > 0 && dim > 0 && seqlen > max_elems / batch / dim)
+    return fail(SSCAN_ERR_INVALID_ARG, "batch*seqlen*dim too large");
+  if ((z == nullptr) != (dz == nullptr)) return fail(SSCAN_ERR_INVALID_ARG, "dz must be given exactly when z is");
+  if (dD && !D) return fail(SSCAN_ERR_INVALID_ARG, "dD requested without D");
+  if (dim > (int64_t(1) << 27)) return fail(SSCAN_ERR_INVALID_ARG, "dim too large for the backward pass");
+  const int64_t N = dstate;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (batch == 0 || dim == 0) return ok();
+  if (!dA) return fail(SSCAN_ERR_INVALID_ARG, "null required pointer (dA)");
+  const size_t es = dtype == SSCAN_BF16 ? 2 : 4;
+  if (seqlen == 0) {
+    // no steps: every gradient is zero except dh0 = dLoss/d(last state)
+    hipError_t e = sscan::launch_fill_state(dA, nullptr, dim * N, s);
+    if (e == hipSuccess && dD) e = sscan::launch_fill_state(dD, nullptr, dim, s);
+    if (e == hipSuccess && ddelta_bias) e = sscan::launch_fill_state(ddelta_bias, nullptr, dim, s);
+    if (e == hipSuccess && dinitial_state) e = sscan::launch_fill_state(dinitial_state, dlast_state, batch * dim * N, s);
+    if (e != hipSuccess) return hip_fail(e, "fill launch");
+    return ok();
+  }
+  if (!x || !delta || !A || !B || !C || !dy || !dx || !ddelta || !dB || !dC)
+    return fail(SSCAN_ERR_INVALID_ARG,
+                "null required pointer (x, delta, A, B, C, dy, dx, ddelta, dA, dB and dC are required)");
+  const void* tok_ptrs[] = {x, delta, z, dy, dx, ddelta, dz, B, C, dB, dC};
+  for (const void* q : tok_ptrs)
+    if (q && !aligned(q, es)) return fail(SSCAN_ERR_INVALID_ARG, "token tensor not aligned to its element size");
+  const void* f32_ptrs[] = {A, D, delta_bias, initial_state, dlast_state, dA, dD, ddelta_bias, dinitial_state};
+  for (const void* q : f32_ptrs)
+    if (q && !aligned(q, 4)) return fail(SSCAN_ERR_INVALID_ARG, "float32 tensor not 4-byte aligned");
+  if (!workspace || !aligned(workspace, 256))
+    return fail(SSCAN_ERR_INVALID_ARG, "workspace missing or not 256-byte aligned");
+  const BwdLayout lo = bwd_layout(batch, seqlen, dim, N);
+  if (workspace_bytes < lo.total)
+    return fail(SSCAN_ERR_INVALID_ARG, "workspace too small (%zu < %zu bytes)", workspace_bytes, lo.total);
+
+  const size_t tok = static_cast<size_t>(batch) * seqlen * dim * es;
+  const size_t bc = static_cast<size_t>(batch) * seqlen * N * es;
+  const size_t st = static_cast<size_t>(batch) * dim * N * 4;
+  struct Buf { const void* p; size_t n; };
+  const Buf inputs[] = {{x, tok}, {delta, tok}, {z, tok}, {dy, tok}, {B, bc}, {C, bc}, {A, size_t(dim) * N * 4},
+                        {D, size_t(dim) * 4}, {delta_bias, size_t(dim) * 4}, {initial_state, st},
+                        {dlast_state, st}};
+  const Buf outputs[] = {{dx, tok}, {ddelta, tok}, {dz, tok}, {dB, bc}, {dC, bc}, {dA, size_t(dim) * N * 4},
+                         {dD, size_t(dim) * 4}, {ddelta_bias, size_t(dim) * 4}, {dinitial_state, st},
+                         {workspace, lo.total}};
+  for (const Buf& o : outputs) {
+    for (const Buf& i : inputs)
+      if (overlaps(o.p, o.n, i.p, i.n)) return fail(SSCAN_ERR_INVALID_ARG, "an output overlaps an input");
+    for (const Buf& o2 : outputs)
+      if (&o2 != &o && overlaps(o.p, o.n, o2.p, o2.n)) return fail(SSCAN_ERR_INVALID_ARG, "outputs overlap");
+  }
+
+  char* ws = static_cast<char*>(workspace);
+  const bool bf16 = dtype == SSCAN_BF16;
+  const bool euler = (flags & SSCAN_FLAG_EULER) != 0;
+  const int64_t nblk = (seqlen + sscan::kBwdBlock - 1) / sscan::kBwdBlock;
+  const int64_t ndt = (dim + sscan::kTile - 1) / sscan::kTile;
+  float* ckpt = reinterpret_cast<float*>(ws + lo.ckpt);
+
+  // 1. checkpoints: the forward recurrence, storing the state entering every chunk
+  sscan::FwdParams p{};
+  p.x = x; p.dt = delta; p.z = nullptr; p.B = B; p.C = C;
+  p.A = A; p.Dskip = nullptr; p.bias = delta_bias;
+  p.y = nullptr; p.h_last = nullptr;
+  p.batch = batch; p.L = seqlen; p.dim = dim; p.N = static_cast<int>(N);
+  p.ndtiles = ndt; p.nblk = nblk;
+  p.seg_len = lo.seg_len; p.nseg = lo.nseg;
+  p.euler = euler;
+  p.ckpt = ckpt;
+  hipError_t e;
+  if (lo.nseg == 1) {
+    p.h_init = initial_state;
+  } else {
+    const int64_t bdn = batch * dim * N;
+    float* sw = reinterpret_cast<float*>(ws + lo.seg);
+    float* carry = sw;
+    p.agg_h = sw + lo.nseg * bdn;
+    p.agg_s = sw + 2 * lo.nseg * bdn;
+    e = sscan::launch_fwd_aggregate(p, bf16, s);
+    if (e != hipSuccess) return hip_fail(e, "segment aggregate launch");
+    e = sscan::launch_fwd_carry(p.agg_h, p.agg_s, A, initial_state, carry, batch, dim, static_cast<int>(N),
+                                lo.nseg, s);
+    if (e != hipSuccess) return hip_fail(e, "segment carry launch");
+    p.h_init = carry;
+  }
+  e = sscan::launch_fwd_checkpoints(p, bf16, s);
+  if (e != hipSuccess) return hip_fail(e, "checkpoint launch");
+
+  // 2. reverse pass and reductions
+  sscan::BwdParams q{};
+  q.x = x; q.dt = delta; q.z = z; q.B = B; q.C = C; q.dy = dy;
+  q.A = A; q.Dskip = D; q.bias = delta_bias; q.dlast = dlast_state; q.ckpt = ckpt;
+  q.dx = dx; q.ddt = ddelta; q.dz = dz;
+  q.gB_part = reinterpret_cast<float*>(ws + lo.gB);
+  q.gC_part = reinterpret_cast<float*>(ws + lo.gC);
+  q.gA_part = reinterpret_cast<float*>(ws + lo.gA);
+  q.gD_part = reinterpret_cast<float*>(ws + lo.gD);
+  q.gbias_part = reinterpret_cast<float*>(ws + lo.gb);
+  q.dh0 = dinitial_state;
+  q.dB = dB; q.dC = dC; q.dA = dA; q.dD = dD; q.dbias = ddelta_bias;
+  q.batch = batch; q.L = seqlen; q.dim = dim; q.ndtiles = ndt; q.nblk = nblk;
+  q.N = static_cast<int>(N);
+  q.euler = euler;
+  e = sscan::launch_bwd(q, bf16, s);
+  if (e != hipSuccess) return hip_fail(e, "backward launch");
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -265,6 +412,23 @@ int sscan_step(int64_t batch, int64_t dim, int64_t dstate, int dtype, unsigned i
   hipError_t e = sscan::launch_step(p, dtype == SSCAN_BF16, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "step launch");
   return ok();
+}
+
+size_t sscan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype) {
+  (void)dtype;
+  if (batch <= 0 || seqlen <= 0 || dim <= 0 || dstate < 1 || dstate > SSCAN_MAX_DSTATE) return 0;
+  return bwd_layout(batch, seqlen, dim, dstate).total;
+}
+
+int sscan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype, unsigned int flags,
+              const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
+              const void* z, const float* delta_bias, const float* initial_state, const void* dy,
+              const float* dlast_state, void* dx, void* ddelta, float* dA, void* dB, void* dC, float* dD,
+              void* dz, float* ddelta_bias, float* dinitial_state, void* workspace, size_t workspace_bytes,
+              void* stream) {
+  return bwd_impl(batch, seqlen, dim, dstate, dtype, flags, x, delta, A, B, C, D, z, delta_bias, initial_state, dy,
+                  dlast_state, dx, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dinitial_state, workspace,
+                  workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -1,0 +1,504 @@
+// Backward pass of the selective scan on gfx950: gradients of a scalar loss with
+// respect to x, dt, z, A, B, C, D, the step-size bias and the initial state.
+//
+// The forward definition (velog.io Mamba review, "Discretization" and section 3.2;
+// page-3 report sections 3 and 4.2) differentiated by the chain rule and run
+// backwards in time: the reverse recurrence the page-3 report's pscan_rev serves
+// (section 4.1), with the forward intermediates recomputed rather than stored (the
+// recomputation that the lengnian.github.io notes, "Part3: Mamba - A Selective SSM",
+// list in the hardware-aware algorithm).
+// Per batch row and channel, with g_l the gradient reaching the state h_l:
+//   g_l     = gyo_l C_l + Abar_{l+1} g_{l+1},   gyo_l = dy_l silu(z_l)
+//   dx_l    = gyo_l D + sum_n g_l phi_l B_l,    dB_l = sum_d g_l phi_l x_l,
+//   dC_l    = sum_d gyo_l h_l,                  dz_l = dy_l yo_l silu'(z_l)
+//   dDelta  = sum_n g_l (A Abar h_{l-1} + dphi/dDelta B_l x_l),  ddt = dDelta sigmoid(dt + bias)
+//   dA      = sum_{b,l} g_l (Delta Abar h_{l-1} + dphi/dA B_l x_l)
+// with phi = Bbar / B: (Abar - 1)/A for the zero-order hold (dphi/dDelta = Abar,
+// dphi/dA = (Delta Abar - phi)/A, evaluated by its Taylor series in u = Delta A when
+// |u| < 0.5), Delta for the Euler rule (dphi/dDelta = 1, dphi/dA = 0).
+//
+// Work decomposition: a workgroup owns (batch row, 64-channel tile); lane =
+// channel, and each wave owns four states (a wave's sums over its states are
+// formed in registers, so only one partial per wave crosses LDS).  A checkpoint pass of the
+// forward kernel has stored the state entering every 16-step block.  The workgroup
+// walks the blocks from last to first; per block:
+//   P1  each wave loads its timesteps' x, dt, z, dy; Delta, x and gyo are staged to
+//       LDS, with the block's B and C rows;
+//   P2  each wave recomputes its state over the block from the checkpoint (the
+//       states kept in registers); C.h goes to LDS for the readout yo, and the
+//       per-channel terms of dC are summed across lanes;
+//   P3  (gate only) each wave forms yo and dz for its timesteps;
+//   P4  each wave runs the reverse recurrence over the block (decays recomputed),
+//       writing its terms of dx and dDelta to LDS, accumulating dA, and summing the
+//       terms of dB across lanes;
+//   P5  each wave sums the terms over states for its timesteps and stores dx, ddt.
+// dB and dC leave as per-tile partial sums, dA, dD and dbias as per-batch-row
+// partial sums; small reduction kernels finish them in a fixed order.
+#include "sscan_device.h"
+#include "sscan_internal.h"
+
+namespace sscan {
+
+namespace {
+
+__device__ __forceinline__ int64_t bwd_xcd_remap(int64_t bid, int64_t nblk) {
+  constexpr int64_t kXcd = 8;
+  const int64_t per = nblk / kXcd, rem = nblk % kXcd;
+  const int64_t xcd = bid % kXcd, slot = bid / kXcd;
+  return (xcd < rem) ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+}
+
+// Value of v in the lane that DPP control CTRL selects (a permutation within rows).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppRowRor8 = 0x128;        // lane i <- row lane (i + 8) mod 16: partner i ^ 8
+constexpr int kDppRowHalfMirror = 0x141;  // lane i <- 7 - i within each 8 lanes: partner i ^ 7
+constexpr int kDppQuadXor2 = 0x4e;        // quad_perm [2,3,0,1]
+constexpr int kDppQuadXor1 = 0xb1;        // quad_perm [1,0,3,2]
+
+// One halving step of a butterfly reduce-scatter through a DPP permutation that
+// pairs every lane with a partner whose BIT differs: lanes with BIT clear keep
+// elements [0, half), the others [half, 2 half), each summed over the pair.
+template <int CTRL, int BIT, int HALF>
+__device__ __forceinline__ void halve_dpp(float* v, int lane) {
+  const bool upper = (lane & BIT) != 0;
+#pragma unroll
+  for (int k = 0; k < HALF; ++k) {
+    const float keep = upper ? v[k + HALF] : v[k];
+    const float send = upper ? v[k] : v[k + HALF];
+    v[k] = keep + dpp<CTRL>(send);
+  }
+}
+
+// Sum of v[0..31] over the 64 lanes of a wave, as a reduce-scatter: afterwards
+// lane L holds in v[0] the total of element L >> 1 (both lanes of a pair agree).
+// The two wide steps use the gfx950 half-swaps (lane i <-> i ^ 32, i ^ 16), the
+// narrow ones DPP row permutations: no LDS and no address registers.
+__device__ __forceinline__ void lane_reduce32(float* v, int lane) {
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {   // partner i ^ 32: lanes 0..31 keep k, 32..63 keep k + 16
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[k]), __float_as_uint(v[k + 16]), false, false);
+    v[k] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {    // partner i ^ 16: rows 0 and 2 keep k, rows 1 and 3 keep k + 8
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[k]), __float_as_uint(v[k + 8]), false, false);
+    v[k] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  halve_dpp<kDppRowRor8, 8, 4>(v, lane);
+  halve_dpp<kDppRowHalfMirror, 4, 2>(v, lane);
+  halve_dpp<kDppQuadXor2, 2, 1>(v, lane);
+  v[0] += dpp<kDppQuadXor1>(v[0]);
+}
+
+// (u e^u - e^u + 1) / u^2 by its Taylor series sum_k (k+1) u^k / (k+2)!, |u| < 0.5.
+__device__ __forceinline__ float dphi1_series(float u) {
+  float r = 1.f / 5760.f;
+  r = fmaf(u, r, 1.f / 840.f);
+  r = fmaf(u, r, 1.f / 144.f);
+  r = fmaf(u, r, 1.f / 30.f);
+  r = fmaf(u, r, 1.f / 8.f);
+  r = fmaf(u, r, 1.f / 3.f);
+  return fmaf(u, r, 0.5f);
+}
+
+}  // namespace
+
+// Waves per workgroup of the backward kernel: four states per wave.
+constexpr int kBwdSpw = 4;
+inline int bwd_waves(int N) { return N <= 4 ? 1 : (N <= 8 ? 2 : 4); }
+
+template <typename Tin, int NW, int NFIX, bool EULER>
+__global__ __launch_bounds__(NW * 64) void bwd_kernel(
+    const Tin* __restrict__ xg, const Tin* __restrict__ dtg, const Tin* __restrict__ zg,
+    const Tin* __restrict__ Bg, const Tin* __restrict__ Cg, const Tin* __restrict__ dyg,
+    const float* __restrict__ Ag, const float* __restrict__ Dg, const float* __restrict__ biasg,
+    const float* __restrict__ dlast, const float* __restrict__ ckpt, Tin* __restrict__ dxg,
+    Tin* __restrict__ ddtg, Tin* __restrict__ dzg, float* __restrict__ gBp, float* __restrict__ gCp,
+    float* __restrict__ gAp, float* __restrict__ gDp, float* __restrict__ gbp, float* __restrict__ dh0,
+    BwdShape sh) {
+  constexpr int T = kBwdBlock;        // timesteps per block (one checkpoint each)
+  constexpr int S = kBwdSpw;          // states per wave
+  constexpr int NSP = NW * S;         // states covered (N rounded up)
+  constexpr int TPW = T / NW;         // prologue / epilogue timesteps per wave
+  static_assert(T * S == 32, "a block's terms of one wave fill one 32-value lane reduction");
+  static_assert(T % NW == 0, "block must split evenly over waves");
+
+  // staging of one block, double-buffered (P1 of block j-1 overlaps P5 of block j)
+  __shared__ float s_d2[2][T][kTile];     // Delta * log2(e)
+  __shared__ float s_xv[2][T][kTile];     // x
+  __shared__ float s_go[2][T][kTile];     // gyo = dy * silu(z)
+  __shared__ float4 s_B[2][T][NSP / 4];   // B and C of the block, four states per float4
+  __shared__ float4 s_C[2][T][NSP / 4];
+  // per-wave partial sums over its states: C.h (readout), dx terms, dDelta terms
+  __shared__ float s_r0[NW][T][kTile];
+  __shared__ float s_r1[NW][T][kTile];
+  __shared__ float s_r2[NW][T][kTile];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tid = threadIdx.x;
+
+  const int64_t blk = bwd_xcd_remap(blockIdx.x, sh.ndtiles * sh.batch);
+  const int64_t dtile = blk % sh.ndtiles;
+  const int64_t b = blk / sh.ndtiles;
+  const int64_t L = sh.L, dim = sh.dim;
+  const int N = NFIX > 0 ? NFIX : sh.N;
+  const int dim32 = static_cast<int>(dim);   // T * dim < 2^31 (checked by the host)
+
+  const int64_t d = dtile * kTile + lane;
+  const bool dvalid = d < dim;
+  const int64_t dd = dvalid ? d : dim - 1;
+  const bool hasZ = zg != nullptr;
+  const float bias2 = biasg ? biasg[dd] * kLog2e : 0.f;
+  const float dsk = Dg ? Dg[dd] : 0.f;
+
+  // this wave's states n0 .. n0 + 3; phantom states (n >= N) get A = 0 and stay
+  // out of every output
+  const int n0 = S * w;
+  float An[S], iAn[S], G[S], gA[S];
+  bool anyzero = false;
+#pragma unroll
+  for (int q = 0; q < S; ++q) {
+    const bool have = n0 + q < N;
+    An[q] = have ? Ag[dd * N + n0 + q] : 0.f;
+    iAn[q] = (An[q] != 0.f) ? 1.f / An[q] : 0.f;
+    anyzero = anyzero || (have && An[q] == 0.f);
+    G[q] = (dlast && have && dvalid) ? dlast[(b * dim + d) * N + n0 + q] : 0.f;
+    gA[q] = 0.f;
+  }
+  const bool zeroA = __any(dvalid && anyzero);
+
+  const int64_t tok_b = b * L * dim + dtile * kTile;  // token offset of (b, l = 0, this tile)
+  float e_sig[TPW], e_gz[TPW];                       // epilogue values of this wave's timesteps
+  float accD = 0.f, accBias = 0.f;
+
+  // P1: x, dt, z, dy of this wave's timesteps of block j; Delta, x, gyo to LDS
+  // buffer j & 1 with the block's B and C rows.
+  auto prologue = [&](int64_t j) {
+    const int pb = static_cast<int>(j & 1);
+    const int64_t l0 = j * T;
+    const int cnt = static_cast<int>((L - l0) < T ? (L - l0) : T);
+    const int64_t base = tok_b + l0 * dim;
+    const Tin* __restrict__ xb = xg + base;
+    const Tin* __restrict__ dtb = dtg + base;
+    const Tin* __restrict__ dyb = dyg + base;
+    const Tin* __restrict__ zb = hasZ ? zg + base : nullptr;
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int t = w + NW * i;
+      float xv = 0.f, dtv = 0.f, zv = 0.f, gy = 0.f;
+      if (dvalid && t < cnt) {
+        const int off = t * dim32 + lane;
+        xv = to_f32(xb[off]);
+        dtv = to_f32(dtb[off]);
+        gy = to_f32(dyb[off]);
+        if (hasZ) zv = to_f32(zb[off]);
+      }
+      const float v2 = fmaf(dtv, kLog2e, bias2);
+      float gyo = gy, gz = 0.f;
+      if (hasZ) {
+        const float sg = hw_rcp(1.f + hw_exp2(-zv * kLog2e));
+        gyo = gy * (zv * sg);
+        gz = gy * sg * fmaf(zv, 1.f - sg, 1.f);   // dy * silu'(z)
+      }
+      s_d2[pb][t][lane] = (t < cnt) ? softplus_log2e(v2) : 0.f;
+      s_xv[pb][t][lane] = xv;
+      s_go[pb][t][lane] = gyo;
+      e_gz[i] = gz;
+      e_sig[i] = hw_rcp(1.f + hw_exp2(-v2));  // sigmoid(dt + bias) = softplus'
+    }
+    const Tin* __restrict__ Bb = Bg + (b * L + l0) * N;
+    const Tin* __restrict__ Cb = Cg + (b * L + l0) * N;
+    float* sB = reinterpret_cast<float*>(s_B[pb]);
+    float* sC = reinterpret_cast<float*>(s_C[pb]);
+    for (int i = tid; i < T * NSP; i += NW * 64) {
+      const int t = i / NSP, nn = i - t * NSP;
+      float bv = 0.f, cv = 0.f;
+      if (nn < N && t < cnt) {
+        bv = to_f32(Bb[t * N + nn]);
+        cv = to_f32(Cb[t * N + nn]);
+      }
+      sB[i] = bv;
+      sC[i] = cv;
+    }
+  };
+
+  const int64_t nblk = sh.nblk;
+  if (nblk > 0) prologue(nblk - 1);
+  for (int64_t j = nblk - 1; j >= 0; --j) {
+    const int pb = static_cast<int>(j & 1);
+    const int64_t l0 = j * T;
+    const int cnt = static_cast<int>((L - l0) < T ? (L - l0) : T);
+    const int64_t tok_blk = tok_b + l0 * dim;
+    const int64_t part = (dtile * sh.batch + b) * N * L + l0;   // + n * L + t: partials of dB, dC
+    float h[S];
+    {
+      const float* ck = ckpt + ((b * nblk + j) * N) * dim + dtile * kTile;
+#pragma unroll
+      for (int q = 0; q < S; ++q) h[q] = (n0 + q < N && dvalid) ? ck[(n0 + q) * dim + lane] : 0.f;
+    }
+    __syncthreads();
+
+    // ---- P2: recompute the block's states from the checkpoint; partial C.h of the
+    // readout to LDS; terms of dC summed across lanes ----
+    float hist[S][T];
+    {
+      float red[S * T];
+      auto recompute = [&](auto safe) {
+        constexpr bool SAFE = decltype(safe)::value;
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const float d2 = s_d2[pb][t][lane];
+          const float xv = s_xv[pb][t][lane];
+          const float go = s_go[pb][t][lane];
+          const float4 b4 = s_B[pb][t][w];
+          const float4 c4 = s_C[pb][t][w];
+          const float bq[S] = {b4.x, b4.y, b4.z, b4.w};
+          const float cq[S] = {c4.x, c4.y, c4.z, c4.w};
+          float yo = 0.f;
+#pragma unroll
+          for (int q = 0; q < S; ++q) {
+            const float a = hw_exp2(d2 * An[q]);
+            hist[q][t] = h[q];
+            if constexpr (EULER) {
+              h[q] = fmaf(a, h[q], (d2 * kLn2) * xv * bq[q]);
+            } else if constexpr (!SAFE) {
+              const float k = xv * bq[q] * iAn[q];
+              h[q] = fmaf(a, h[q] + k, -k);
+            } else {
+              const float g = (An[q] != 0.f) ? (a - 1.f) * iAn[q] : d2 * kLn2;
+              h[q] = fmaf(a, h[q], g * bq[q] * xv);
+            }
+            red[q * T + t] = go * h[q];
+            yo = fmaf(cq[q], h[q], yo);
+          }
+          s_r0[w][t][lane] = yo;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      if (EULER || !zeroA)
+        recompute(std::false_type{});
+      else
+        recompute(std::true_type{});
+      lane_reduce32(red, lane);
+      if ((lane & 1) == 0) {
+        const int k = lane >> 1, q = k / T, t = k % T;
+        if (n0 + q < N && t < cnt) gCp[part + (n0 + q) * L + t] = red[0];
+      }
+    }
+
+    // ---- P4: reverse recurrence over the block (decays recomputed); partial sums
+    // of the dx and dDelta terms to LDS, dA accumulated, terms of dB summed across
+    // lanes ----
+    {
+      float red[S * T];
+#pragma unroll
+      for (int t = T - 1; t >= 0; --t) {
+        const float go = s_go[pb][t][lane];
+        const float d2 = s_d2[pb][t][lane];
+        const float xv = s_xv[pb][t][lane];
+        const float4 b4 = s_B[pb][t][w];
+        const float4 c4 = s_C[pb][t][w];
+        const float bq[S] = {b4.x, b4.y, b4.z, b4.w};
+        const float cq[S] = {c4.x, c4.y, c4.z, c4.w};
+        const float delta = d2 * kLn2;
+        float r1 = 0.f, r2 = 0.f;
+#pragma unroll
+        for (int q = 0; q < S; ++q) {
+          const float a = hw_exp2(d2 * An[q]);
+          const float hp = hist[q][t];
+          const float gh = fmaf(go, cq[q], G[q]);
+          const float bx = bq[q] * xv;
+          float phi;
+          if constexpr (EULER) {
+            phi = delta;
+            r2 = fmaf(gh, fmaf(An[q] * a, hp, bx), r2);
+            gA[q] = fmaf(gh, delta * a * hp, gA[q]);
+          } else {
+            phi = (An[q] != 0.f) ? (a - 1.f) * iAn[q] : delta;
+            r2 = fmaf(gh * a, fmaf(An[q], hp, bx), r2);
+            // both forms are computed (each finite everywhere) and blended, so no
+            // per-lane branch splits the step
+            const float u = delta * An[q];
+            const float ser = delta * delta * dphi1_series(fmaxf(fminf(u, 0.5f), -0.5f));
+            const float dir = (delta * a - phi) * iAn[q];
+            const float wsel = (fabsf(u) < 0.5f) ? 1.f : 0.f;
+            const float dphi_dA = fmaf(wsel, ser - dir, dir);
+            gA[q] = fmaf(gh, fmaf(delta * a, hp, dphi_dA * bx), gA[q]);
+          }
+          const float gphi = gh * phi;
+          red[q * T + t] = gphi * xv;
+          r1 = fmaf(gphi, bq[q], r1);
+          G[q] = a * gh;
+        }
+        s_r1[w][t][lane] = r1;
+        s_r2[w][t][lane] = r2;
+        // dA is needed only after the last block; without this anchor the compiler
+        // sinks its update out of the step and keeps every step's terms alive
+#pragma unroll
+        for (int q = 0; q < S; ++q) asm volatile("" : "+v"(gA[q]));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      lane_reduce32(red, lane);
+      if ((lane & 1) == 0) {
+        const int k = lane >> 1, q = k / T, t = k % T;
+        if (n0 + q < N && t < cnt) gBp[part + (n0 + q) * L + t] = red[0];
+      }
+    }
+    if (j == 0 && dh0 && dvalid) {
+#pragma unroll
+      for (int q = 0; q < S; ++q)
+        if (n0 + q < N) dh0[(b * dim + d) * N + n0 + q] = G[q];
+    }
+    __syncthreads();
+
+    // ---- P5: sums over states; store dz, dx, ddt.  Then P1 of the next block into
+    // the other staging buffer ----
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int t = w + NW * i;
+      if (dvalid && t < cnt) {
+        const float go = s_go[pb][t][lane];
+        const float xv = s_xv[pb][t][lane];
+        float gx = go * dsk, gd = 0.f, yo = dsk * xv;
+#pragma unroll
+        for (int q = 0; q < NW; ++q) {
+          yo += s_r0[q][t][lane];
+          gx += s_r1[q][t][lane];
+          gd += s_r2[q][t][lane];
+        }
+        const float gdt = gd * e_sig[i];
+        const int off = t * dim32 + lane;
+        if (hasZ) store_val(&(dzg + tok_blk)[off], e_gz[i] * yo);
+        store_val(&(dxg + tok_blk)[off], gx);
+        store_val(&(ddtg + tok_blk)[off], gdt);
+        accD = fmaf(go, xv, accD);
+        accBias += gdt;
+      }
+    }
+    if (j > 0) prologue(j - 1);
+  }
+
+  // per-batch-row partial sums of dA, dD and dbias
+  if (dvalid) {
+#pragma unroll
+    for (int q = 0; q < S; ++q)
+      if (n0 + q < N) gAp[(b * N + n0 + q) * dim + d] = gA[q];
+  }
+  __syncthreads();
+  s_r1[w][0][lane] = accD;
+  s_r2[w][0][lane] = accBias;
+  __syncthreads();
+  if (w == 0 && dvalid) {
+    float sD = 0.f, sb = 0.f;
+#pragma unroll
+    for (int q = 0; q < NW; ++q) {
+      sD += s_r1[q][0][lane];
+      sb += s_r2[q][0][lane];
+    }
+    gDp[b * dim + d] = sD;
+    gbp[b * dim + d] = sb;
+  }
+}
+
+// dB[b][l][n] = sum over channel tiles of the partials (fixed order), in the token dtype.
+template <typename Tin>
+__global__ __launch_bounds__(256) void bwd_reduce_bc(const float* __restrict__ gBp, const float* __restrict__ gCp,
+                                                     Tin* __restrict__ dB, Tin* __restrict__ dC, int64_t batch,
+                                                     int64_t L, int N, int64_t ndtiles) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= batch * L) return;
+  const int64_t b = i / L, l = i - b * L;
+  for (int n = 0; n < N; ++n) {
+    float sB = 0.f, sC = 0.f;
+    for (int64_t k = 0; k < ndtiles; ++k) {
+      const int64_t off = ((k * batch + b) * N + n) * L + l;
+      sB += gBp[off];
+      sC += gCp[off];
+    }
+    store_val(&dB[i * N + n], sB);
+    store_val(&dC[i * N + n], sC);
+  }
+}
+
+// dA[d][n], dD[d], dbias[d] = sums over batch rows of the partials (fixed order).
+__global__ __launch_bounds__(256) void bwd_reduce_params(const float* __restrict__ gAp, const float* __restrict__ gDp,
+                                                         const float* __restrict__ gbp, float* __restrict__ dA,
+                                                         float* __restrict__ dD, float* __restrict__ dbias,
+                                                         int64_t batch, int64_t dim, int N) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= dim * N) return;
+  const int64_t d = i / N;
+  const int n = static_cast<int>(i - d * N);
+  float s = 0.f;
+  for (int64_t b = 0; b < batch; ++b) s += gAp[(b * N + n) * dim + d];
+  dA[i] = s;
+  if (n == 0) {
+    float sD = 0.f, sb = 0.f;
+    for (int64_t b = 0; b < batch; ++b) {
+      sD += gDp[b * dim + d];
+      sb += gbp[b * dim + d];
+    }
+    if (dD) dD[d] = sD;
+    if (dbias) dbias[d] = sb;
+  }
+}
+
+namespace {
+
+template <typename Tin, int NW, int NF, bool EU>
+void launch_bwd_one(const BwdParams& p, hipStream_t s) {
+  BwdShape sh{p.batch, p.L, p.dim, p.ndtiles, p.nblk, p.N};
+  hipLaunchKernelGGL((bwd_kernel<Tin, NW, NF, EU>), dim3(static_cast<unsigned>(p.ndtiles * p.batch)),
+                     dim3(NW * 64), 0, s, static_cast<const Tin*>(p.x), static_cast<const Tin*>(p.dt),
+                     static_cast<const Tin*>(p.z), static_cast<const Tin*>(p.B), static_cast<const Tin*>(p.C),
+                     static_cast<const Tin*>(p.dy), p.A, p.Dskip, p.bias, p.dlast, p.ckpt, static_cast<Tin*>(p.dx),
+                     static_cast<Tin*>(p.ddt), static_cast<Tin*>(p.dz), p.gB_part, p.gC_part, p.gA_part,
+                     p.gD_part, p.gbias_part, p.dh0, sh);
+}
+
+template <typename Tin, bool EU>
+void launch_bwd_n(const BwdParams& p, hipStream_t s) {
+  switch (bwd_waves(p.N)) {
+    case 1: launch_bwd_one<Tin, 1, 0, EU>(p, s); break;
+    case 2: launch_bwd_one<Tin, 2, 0, EU>(p, s); break;
+    default:
+      if (p.N == 16)
+        launch_bwd_one<Tin, 4, 16, EU>(p, s);
+      else
+        launch_bwd_one<Tin, 4, 0, EU>(p, s);
+      break;
+  }
+}
+
+template <typename Tin>
+hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
+  if (p.euler)
+    launch_bwd_n<Tin, true>(p, s);
+  else
+    launch_bwd_n<Tin, false>(p, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t nbl = p.batch * p.L;
+  hipLaunchKernelGGL((bwd_reduce_bc<Tin>), dim3(static_cast<unsigned>((nbl + 255) / 256)), dim3(256), 0, s,
+                     p.gB_part, p.gC_part, static_cast<Tin*>(p.dB), static_cast<Tin*>(p.dC), p.batch, p.L, p.N,
+                     p.ndtiles);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t ndn = p.dim * p.N;
+  hipLaunchKernelGGL(bwd_reduce_params, dim3(static_cast<unsigned>((ndn + 255) / 256)), dim3(256), 0, s, p.gA_part,
+                     p.gD_part, p.gbias_part, p.dA, p.dD, p.dbias, p.batch, p.dim, p.N);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdParams& p, bool bf16, hipStream_t s) {
+  if (p.batch <= 0 || p.dim <= 0) return hipSuccess;
+  return bf16 ? launch_bwd_t<bf16_t>(p, s) : launch_bwd_t<float>(p, s);
+}
+
+}  // namespace sscan

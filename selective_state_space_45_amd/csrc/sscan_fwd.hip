@@ -111,15 +111,21 @@ __device__ __forceinline__ int64_t after(int64_t v, float dep) {
 }
 
 // One workgroup: (batch row b, 64-channel tile, segment); NSPLIT waves x NPW states.
+// MODE: kFwdOut (y and the final state), kFwdAgg (segment aggregates only: end state
+// from a zero start and sum of Delta), kFwdCkpt (no y: the state entering every
+// block of kBwdBlock steps is written to ckpt, for the backward pass).
 // NFIX: N as a compile-time constant (0 = read it from the shape at run time).
 // EULER: Bbar = Delta B instead of the zero-order hold.
-template <typename Tin, int NSPLIT, int NPW, bool AGG, bool PAIR, int NFIX, bool EULER>
+template <typename Tin, int NSPLIT, int NPW, int MODE, bool PAIR, int NFIX, bool EULER>
 __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
     const Tin* __restrict__ xg, const Tin* __restrict__ dtg, const Tin* __restrict__ zg,
     const Tin* __restrict__ Bg, const Tin* __restrict__ Cg, const float* __restrict__ Ag,
     const float* __restrict__ Dg, const float* __restrict__ biasg, const float* __restrict__ h_init,
     Tin* __restrict__ yg, float* __restrict__ h_last, float* __restrict__ agg_h, float* __restrict__ agg_s,
-    FwdShape sh) {
+    float* __restrict__ ckpt, FwdShape sh) {
+  constexpr bool AGG = MODE == kFwdAgg;
+  constexpr bool OUT = MODE == kFwdOut;
+  constexpr bool CKPT = MODE == kFwdCkpt;
   constexpr int T = kChunk;
   constexpr int TPW = T / NSPLIT;  // prologue/epilogue timesteps per wave per chunk
   constexpr int H = T / 2;
@@ -132,7 +138,7 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
   __shared__ float s_xv[2][T][kTile];
   // States after each timestep, for the readout C.h done by the epilogue wave.
   constexpr int NS = NSPLIT * NPW;
-  __shared__ float s_h[AGG ? 1 : 2][AGG ? 1 : NS][T][kTile];
+  __shared__ float s_h[OUT ? 2 : 1][OUT ? NS : 1][T][kTile];
   __shared__ float s_red[AGG ? NSPLIT : 1][kTile];
 
   const int lane = threadIdx.x & 63;
@@ -222,7 +228,7 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
         if (dvalid) {
           a = (Xb + off)[lane];
           e = (DTb + off)[lane];
-          if (!AGG && hasZ) f = (Zb + off)[lane];
+          if (OUT && hasZ) f = (Zb + off)[lane];
         }
       }
       rx[i] = a;
@@ -268,7 +274,7 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
         const float tk = ssum + yk;
         scomp = (tk - ssum) - yk;
         ssum = tk;
-      } else {
+      } else if constexpr (OUT) {
         eg[P][i] = hasZ ? silu(to_f32(rz[i])) : 1.f;
         ed[P][i] = dsk * xv;
       }
@@ -288,7 +294,7 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
 #pragma unroll
         for (int j = 0; j < NPW; ++j) {
           h[j] = fmaf(ea[t][j], h[j], vx[t].y * bc[t].get(j, sel));
-          if constexpr (!AGG) s_h[P][n0 + j][t][lane] = h[j];
+          if constexpr (OUT) s_h[P][n0 + j][t][lane] = h[j];
         }
       }
     } else if (!zeroA) {
@@ -299,7 +305,7 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
           const float q = bc[t].get(j, sel) * iAj[j];
           const float k = vx[t].y * q;
           h[j] = fmaf(ea[t][j], h[j] + k, -k);
-          if constexpr (!AGG) s_h[P][n0 + j][t][lane] = h[j];
+          if constexpr (OUT) s_h[P][n0 + j][t][lane] = h[j];
         }
       }
     } else {
@@ -310,7 +316,7 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
         for (int j = 0; j < NPW; ++j) {
           const float g = live[j] * ((Aj[j] != 0.f) ? (ea[t][j] - 1.f) * iAj[j] : dl);
           h[j] = fmaf(ea[t][j], h[j], g * bc[t].get(j, sel) * vx[t].y);
-          if constexpr (!AGG) s_h[P][n0 + j][t][lane] = h[j];
+          if constexpr (OUT) s_h[P][n0 + j][t][lane] = h[j];
         }
       }
     }
@@ -321,7 +327,7 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
   // loads.  g, dx: silu(z) and D*x of the same timesteps.
   auto epilogue = [&](auto pc, int c, const float* g, const float* dx) {
     constexpr int P = decltype(pc)::value;
-    if constexpr (!AGG) {
+    if constexpr (OUT) {
 #pragma unroll
       for (int i = 0; i < TPW; ++i) {
         const int t = w + NSPLIT * i;
@@ -386,14 +392,29 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
       bcload_tail(c, vx[T - 1].y);
     else
       bcload_full(c, Par<1>{}, vx[T - 1].y);
+    // state entering each half of the chunk: [batch][block][N][dim], block = index of
+    // the kBwdBlock-step block in the sequence (two per chunk)
+    static_assert(!CKPT || 2 * kBwdBlock == T, "checkpoints are taken at half chunks");
+    auto checkpoint = [&](int half) {
+      if constexpr (CKPT) {
+        const int64_t blk = 2 * (l_begin / T + c) + half;
+        if (dvalid && blk < sh.nblk) {
+#pragma unroll
+          for (int j = 0; j < NPW; ++j)
+            if (have[j]) ckpt[((b * sh.nblk + blk) * N + n0 + j) * dim + d] = h[j];
+        }
+      }
+    };
+    checkpoint(0);
     run_steps(pc, Par<0>{}, vx, ea);
     __builtin_amdgcn_sched_barrier(0);
-    if (!AGG && c >= 1) epilogue(Par<Q>{}, c - 1, pg, pd);
+    if (OUT && c >= 1) epilogue(Par<Q>{}, c - 1, pg, pd);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (!TAIL) {
       if (c + 1 < nfull) bcload_full(c + 1, Par<0>{}, h[0]);
     }
     __builtin_amdgcn_sched_barrier(0);
+    checkpoint(1);
     run_steps(pc, Par<1>{}, vx, ea);
     __syncthreads();
   };
@@ -435,7 +456,7 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
       for (int q = 0; q < NSPLIT; ++q) s += s_red[q][lane];
       agg_s[(static_cast<int64_t>(seg) * sh.batch + b) * dim + d] = s;
     }
-  } else {
+  } else if constexpr (OUT) {
     if (h_last && seg == sh.nseg - 1 && dvalid) {
       float* hl = h_last + (b * dim + d) * N;
 #pragma unroll
@@ -483,61 +504,67 @@ int fwd_nsplit(int N) {
 
 namespace {
 
-template <typename Tin, int NS, bool AGG, bool PR, int NF, bool EU>
+template <typename Tin, int NS, int MODE, bool PR, int NF, bool EU>
 void launch_one(const FwdParams& p, dim3 grid, hipStream_t s) {
-  FwdShape sh{p.batch, p.L, p.dim, p.seg_len, p.ndtiles, p.N, p.nseg};
-  hipLaunchKernelGGL((fwd_kernel<Tin, NS, 1, AGG, PR, NF, EU>), grid, dim3(NS * 64), 0, s,
+  FwdShape sh{p.batch, p.L, p.dim, p.seg_len, p.ndtiles, p.nblk, p.N, p.nseg};
+  hipLaunchKernelGGL((fwd_kernel<Tin, NS, 1, MODE, PR, NF, EU>), grid, dim3(NS * 64), 0, s,
                      static_cast<const Tin*>(p.x), static_cast<const Tin*>(p.dt), static_cast<const Tin*>(p.z),
                      static_cast<const Tin*>(p.B), static_cast<const Tin*>(p.C), p.A, p.Dskip, p.bias, p.h_init,
-                     static_cast<Tin*>(p.y), p.h_last, p.agg_h, p.agg_s, sh);
+                     static_cast<Tin*>(p.y), p.h_last, p.agg_h, p.agg_s, p.ckpt, sh);
 }
 
-template <typename Tin, bool AGG, bool PR, bool EU>
+template <typename Tin, int MODE, bool PR, bool EU>
 void launch_by_n(const FwdParams& p, dim3 grid, hipStream_t s) {
   switch (fwd_nsplit(p.N)) {
-    case 1: launch_one<Tin, 1, AGG, PR, 0, EU>(p, grid, s); break;
-    case 2: launch_one<Tin, 2, AGG, PR, 0, EU>(p, grid, s); break;
-    case 4: launch_one<Tin, 4, AGG, PR, 0, EU>(p, grid, s); break;
-    case 8: launch_one<Tin, 8, AGG, PR, 0, EU>(p, grid, s); break;
+    case 1: launch_one<Tin, 1, MODE, PR, 0, EU>(p, grid, s); break;
+    case 2: launch_one<Tin, 2, MODE, PR, 0, EU>(p, grid, s); break;
+    case 4: launch_one<Tin, 4, MODE, PR, 0, EU>(p, grid, s); break;
+    case 8: launch_one<Tin, 8, MODE, PR, 0, EU>(p, grid, s); break;
     default:
       if (p.N == 16)
-        launch_one<Tin, 16, AGG, PR, 16, EU>(p, grid, s);
+        launch_one<Tin, 16, MODE, PR, 16, EU>(p, grid, s);
       else
-        launch_one<Tin, 16, AGG, PR, 0, EU>(p, grid, s);
+        launch_one<Tin, 16, MODE, PR, 0, EU>(p, grid, s);
       break;
   }
 }
 
-template <typename Tin, bool AGG, bool PR>
+template <typename Tin, int MODE, bool PR>
 void launch_by_rule(const FwdParams& p, dim3 grid, hipStream_t s) {
   if (p.euler)
-    launch_by_n<Tin, AGG, PR, true>(p, grid, s);
+    launch_by_n<Tin, MODE, PR, true>(p, grid, s);
   else
-    launch_by_n<Tin, AGG, PR, false>(p, grid, s);
+    launch_by_n<Tin, MODE, PR, false>(p, grid, s);
 }
 
-template <bool AGG>
+template <int MODE>
 hipError_t launch_fwd_impl(const FwdParams& p, bool bf16, hipStream_t s) {
-  const int64_t nblocks = p.ndtiles * p.batch * (AGG ? (p.nseg - 1) : p.nseg);
+  const int64_t nblocks = p.ndtiles * p.batch * (MODE == kFwdAgg ? (p.nseg - 1) : p.nseg);
   if (nblocks <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(nblocks));
   const bool pair = bf16 && (p.N % 2 == 0) && ((reinterpret_cast<uintptr_t>(p.B) & 3) == 0) &&
                     ((reinterpret_cast<uintptr_t>(p.C) & 3) == 0);
   if (!bf16)
-    launch_by_rule<float, AGG, false>(p, grid, s);
+    launch_by_rule<float, MODE, false>(p, grid, s);
   else if (pair)
-    launch_by_rule<bf16_t, AGG, true>(p, grid, s);
+    launch_by_rule<bf16_t, MODE, true>(p, grid, s);
   else
-    launch_by_rule<bf16_t, AGG, false>(p, grid, s);
+    launch_by_rule<bf16_t, MODE, false>(p, grid, s);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_fwd_main(const FwdParams& p, bool bf16, hipStream_t s) { return launch_fwd_impl<false>(p, bf16, s); }
+hipError_t launch_fwd_main(const FwdParams& p, bool bf16, hipStream_t s) {
+  return launch_fwd_impl<kFwdOut>(p, bf16, s);
+}
 
 hipError_t launch_fwd_aggregate(const FwdParams& p, bool bf16, hipStream_t s) {
-  return launch_fwd_impl<true>(p, bf16, s);
+  return launch_fwd_impl<kFwdAgg>(p, bf16, s);
+}
+
+hipError_t launch_fwd_checkpoints(const FwdParams& p, bool bf16, hipStream_t s) {
+  return launch_fwd_impl<kFwdCkpt>(p, bf16, s);
 }
 
 hipError_t launch_fwd_carry(const float* agg_h, const float* agg_s, const float* A, const float* h_init, float* carry,

@@ -8,6 +8,12 @@ namespace sscan {
 
 constexpr int kTile = 64;     // channels per workgroup: one per lane of a wave
 constexpr int kChunk = 16;    // timesteps staged through LDS per chunk
+constexpr int kBwdBlock = 8;  // timesteps per backward block = checkpoint spacing
+
+// Modes of the forward kernel.
+constexpr int kFwdOut = 0;    // y (and the final state)
+constexpr int kFwdAgg = 1;    // per-segment aggregates for the two-level scan
+constexpr int kFwdCkpt = 2;   // states entering every kBwdBlock steps, for the backward pass
 
 struct FwdParams {
   const void* x;
@@ -23,6 +29,8 @@ struct FwdParams {
   float* h_last;          // nullable, written by the last segment
   float* agg_h;           // aggregate pass: [nseg][batch][dim][N] local end state
   float* agg_s;           // aggregate pass: [nseg][batch][dim]    sum of Delta*log2(e)
+  float* ckpt;            // checkpoint pass: [batch][nblk][N][dim] state entering each block
+  int64_t nblk;           // backward blocks over the whole sequence: ceil(L / kBwdBlock)
   int64_t batch, L, dim;
   int64_t seg_len;        // timesteps per segment (multiple of kChunk unless nseg == 1)
   int64_t ndtiles;        // ceil(dim / kTile)
@@ -34,7 +42,7 @@ struct FwdParams {
 // Sizes passed by value to the forward kernels (pointers go as separate
 // restrict-qualified arguments so the compiler can keep B/C loads scalar).
 struct FwdShape {
-  int64_t batch, L, dim, seg_len, ndtiles;
+  int64_t batch, L, dim, seg_len, ndtiles, nblk;
   int N, nseg;
 };
 
@@ -54,12 +62,52 @@ struct StepParams {
   bool euler;             // Bbar = Delta * B instead of the zero-order hold
 };
 
+// Backward pass.  Workspace regions are carved by the host (sscan_api.hip).
+struct BwdParams {
+  const void* x;
+  const void* dt;
+  const void* z;          // nullable
+  const void* B;
+  const void* C;
+  const void* dy;
+  const float* A;
+  const float* Dskip;     // nullable
+  const float* bias;      // nullable
+  const float* dlast;     // nullable: dLoss / d(last state) [batch][dim][N]
+  const float* ckpt;      // [batch][nblk][N][dim] state entering each block of kBwdBlock steps
+  void* dx;
+  void* ddt;
+  void* dz;               // nullable (iff z is)
+  float* gB_part;         // [ndtiles][batch][N][L] per channel-tile partial sums
+  float* gC_part;         // [ndtiles][batch][N][L]
+  float* gA_part;         // [batch][N][dim]
+  float* gD_part;         // [batch][dim]
+  float* gbias_part;      // [batch][dim]
+  float* dh0;             // nullable: [batch][dim][N]
+  void* dB;               // [batch][L][N] (token dtype)
+  void* dC;
+  float* dA;              // [dim][N]
+  float* dD;              // nullable
+  float* dbias;           // nullable
+  int64_t batch, L, dim, ndtiles, nblk;
+  int N;
+  bool euler;
+};
+
+struct BwdShape {
+  int64_t batch, L, dim, ndtiles, nblk;
+  int N;
+};
+
+hipError_t launch_bwd(const BwdParams& p, bool bf16, hipStream_t s);
+
 // Waves per workgroup of the forward kernels for a given N (each wave owns one state).
 int fwd_nsplit(int N);
 
 // Launchers; return hipSuccess or the launch error.
 hipError_t launch_fwd_main(const FwdParams& p, bool bf16, hipStream_t s);
 hipError_t launch_fwd_aggregate(const FwdParams& p, bool bf16, hipStream_t s);
+hipError_t launch_fwd_checkpoints(const FwdParams& p, bool bf16, hipStream_t s);
 hipError_t launch_fwd_carry(const float* agg_h, const float* agg_s, const float* A, const float* h_init,
                             float* carry, int64_t batch, int64_t dim, int N, int nseg, hipStream_t s);
 hipError_t launch_fill_state(float* dst, const float* src, int64_t n, hipStream_t s);

@@ -24,6 +24,9 @@ def lib():
     lb.sscan_last_error.restype = ctypes.c_char_p
     lb.sscan_fwd_workspace_size.argtypes = [I64, I64, I64, I64, ctypes.c_int]
     lb.sscan_fwd_workspace_size.restype = SZ
+    lb.sscan_bwd_workspace_size.argtypes = [I64, I64, I64, I64, ctypes.c_int]
+    lb.sscan_bwd_workspace_size.restype = SZ
+    lb.sscan_bwd.argtypes = [I64, I64, I64, I64, ctypes.c_int, U32] + [P] * 21 + [SZ, P]
     return lb
 
 
@@ -36,7 +39,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for must in ("sscan_fwd", "sscan_step", "sscan_fwd_segmented", "sscan_fwd_workspace_size",
-                 "sscan_last_error", "sscan_version"):
+                 "sscan_bwd", "sscan_bwd_workspace_size", "sscan_last_error", "sscan_version"):
         assert must in names
 
 
@@ -135,3 +138,37 @@ def test_workspace_size(lib):
     ws = lib.sscan_fwd_workspace_size(1, 131072, 2560, 16, 1)
     assert ws > 0 and ws % (4 * 2560 * 33) == 0
     assert lib.sscan_fwd_workspace_size(1, 0, 2560, 16, 1) == 0
+
+
+def bwd(lib, batch=2, L=8, dim=4, N=4, dtype=0, flags=0, z=None, dz=None, D=None, dD=None, ws=None, wsb=0,
+        x=FAKE):
+    P = ctypes.c_void_p
+    return lib.sscan_bwd(batch, L, dim, N, dtype, flags, x, FAKE2, P(0x30000), P(0x40000), P(0x50000), D, z, None,
+                         None, P(0x60000), None, P(0x70000), P(0x80000), P(0x90000), P(0xa0000), P(0xb0000), dD, dz,
+                         None, None, ws, wsb, None)
+
+
+def test_bwd_validation(lib):
+    P = ctypes.c_void_p
+    assert bwd(lib, N=17) == 2
+    assert bwd(lib, flags=4) == 2
+    assert bwd(lib, z=P(0xc0000)) == 1                 # z without dz
+    assert b"dz" in lib.sscan_last_error()
+    assert bwd(lib, dD=P(0xd0000)) == 1                # dD without D
+    assert bwd(lib) == 1                                # no workspace
+    assert b"workspace" in lib.sscan_last_error()
+    need = lib.sscan_bwd_workspace_size(2, 8, 4, 4, 0)
+    assert need > 0
+    assert bwd(lib, ws=P(0x1000000), wsb=need - 1) == 1
+    assert b"too small" in lib.sscan_last_error()
+    assert bwd(lib, x=None, ws=P(0x1000000), wsb=need) == 1
+    assert bwd(lib, batch=0) == 0
+
+
+def test_bwd_workspace_size_grows_with_the_problem(lib):
+    a = lib.sscan_bwd_workspace_size(8, 4096, 2048, 16, 1)
+    # checkpoints (one state per 8 steps) + partials of dB, dC per channel tile + parameter partials
+    ckpt = 8 * (4096 // 8) * 16 * 2048 * 4
+    parts = 2 * 32 * 8 * 16 * 4096 * 4
+    assert a >= ckpt + parts
+    assert lib.sscan_bwd_workspace_size(8, 0, 2048, 16, 1) == 0

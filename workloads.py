@@ -246,6 +246,19 @@ def fwd_algorithmic_bytes(batch, seqlen, dim, dstate, dtype, with_z=True, with_D
     return tok + bc + par + st
 
 
+def bwd_algorithmic_bytes(batch: int, seqlen: int, dim: int, dstate: int, dtype: str,
+                          with_z: bool = True, with_D: bool = True, with_bias: bool = True) -> int:
+    """Bytes the backward pass must move: x, dt, (z), dy read and dx, ddt, (dz) written
+    once per (b, l, d); B, C read and dB, dC written once per (b, l, n); A, (D), (bias)
+    read and their gradients written once.  Checkpoints and partial sums are not
+    counted (they are the implementation's choice, not the method's)."""
+    s = 2 if dtype == "bf16" else 4
+    tok = batch * seqlen * dim * s * ((4 if with_z else 3) + (3 if with_z else 2))
+    bc = batch * seqlen * dstate * s * 4
+    par = 4 * dim * dstate * 2 + 4 * dim * ((2 if with_D else 0) + (2 if with_bias else 0))
+    return tok + bc + par
+
+
 def step_algorithmic_bytes(batch, dim, dstate, dtype, with_z=True, with_D=True, with_bias=False) -> int:
     """Bytes one decode step must move: state read + written, token tensors, parameters."""
     s = 2 if dtype == "bf16" else 4
