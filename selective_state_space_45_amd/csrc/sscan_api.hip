@@ -209,26 +209,53 @@ int fwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dty
 size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct BwdLayout {
-  size_t ckpt, gB, gC, gA, gD, gb, seg, total;
-  int nseg;
+  size_t ckpt, gB, gC, gA, gD, gb, seg, rg, rs, gin, total;
+  int nseg;                // forward (checkpoint) pass segments
   int64_t seg_len;
+  int bseg;                // reverse pass segments
+  int64_t seg_blocks;      // kBwdBlock-step blocks per reverse segment
 };
+
+// Reverse-pass segments: the reverse kernel has four waves per workgroup and two
+// workgroups fit a CU, so split the sequence until the (batch, channel tile, segment)
+// grid gives about two workgroups per CU, with segments of at least 64 steps.
+int bwd_segments(int64_t batch, int64_t seqlen, int64_t dim) {
+  const int64_t ndt = (dim + sscan::kTile - 1) / sscan::kTile;
+  const int64_t base = ndt * batch;
+  const int64_t cus = device_cus();
+  if (base <= 0) return 1;
+  int64_t want = (2 * cus + base - 1) / base;
+  const int64_t maxseg = seqlen / 64;
+  if (want > maxseg) want = maxseg;
+  if (want > 1024) want = 1024;
+  return want < 1 ? 1 : static_cast<int>(want);
+}
 
 BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t N) {
   BwdLayout lo{};
   const int64_t nblk = (seqlen + sscan::kBwdBlock - 1) / sscan::kBwdBlock;
   const int64_t ndt = (dim + sscan::kTile - 1) / sscan::kTile;
+  const int want = bwd_segments(batch, seqlen, dim);
+  lo.seg_blocks = (nblk + want - 1) / want;
+  if (lo.seg_blocks < 1) lo.seg_blocks = 1;
+  lo.bseg = static_cast<int>((nblk + lo.seg_blocks - 1) / lo.seg_blocks);
+  if (lo.bseg < 1) lo.bseg = 1;
+  const size_t bdn = static_cast<size_t>(batch) * dim * N;
   size_t off = 0;
   lo.ckpt = off; off += round256(static_cast<size_t>(batch) * nblk * N * dim * 4);
   lo.gB = off;   off += round256(static_cast<size_t>(ndt) * batch * N * seqlen * 4);
   lo.gC = off;   off += round256(static_cast<size_t>(ndt) * batch * N * seqlen * 4);
-  lo.gA = off;   off += round256(static_cast<size_t>(batch) * N * dim * 4);
-  lo.gD = off;   off += round256(static_cast<size_t>(batch) * dim * 4);
-  lo.gb = off;   off += round256(static_cast<size_t>(batch) * dim * 4);
+  lo.gA = off;   off += round256(static_cast<size_t>(lo.bseg) * bdn * 4);
+  lo.gD = off;   off += round256(static_cast<size_t>(lo.bseg) * batch * dim * 4);
+  lo.gb = off;   off += round256(static_cast<size_t>(lo.bseg) * batch * dim * 4);
   const SegPlan pl = plan_segments(batch, seqlen, dim, N, 0, ~size_t(0), true);
   lo.nseg = pl.nseg;
   lo.seg_len = pl.seg_len;
   lo.seg = off;  off += round256(seg_workspace_bytes(batch, dim, N, pl.nseg));
+  const size_t nb = lo.bseg > 1 ? static_cast<size_t>(lo.bseg) : 0;
+  lo.rg = off;   off += round256(nb * bdn * 4);
+  lo.rs = off;   off += round256(nb * batch * dim * 4);
+  lo.gin = off;  off += round256(nb * bdn * 4);
   lo.total = off;
   return lo;
 }
@@ -344,6 +371,11 @@ int bwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dty
   q.batch = batch; q.L = seqlen; q.dim = dim; q.ndtiles = ndt; q.nblk = nblk;
   q.N = static_cast<int>(N);
   q.euler = euler;
+  q.nseg = lo.bseg;
+  q.seg_blocks = lo.seg_blocks;
+  q.ragg_g = reinterpret_cast<float*>(ws + lo.rg);
+  q.ragg_s = reinterpret_cast<float*>(ws + lo.rs);
+  q.gin = reinterpret_cast<float*>(ws + lo.gin);
   e = sscan::launch_bwd(q, bf16, s);
   if (e != hipSuccess) return hip_fail(e, "backward launch");
   return ok();

@@ -115,10 +115,10 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(
     const Tin* __restrict__ xg, const Tin* __restrict__ dtg, const Tin* __restrict__ zg,
     const Tin* __restrict__ Bg, const Tin* __restrict__ Cg, const Tin* __restrict__ dyg,
     const float* __restrict__ Ag, const float* __restrict__ Dg, const float* __restrict__ biasg,
-    const float* __restrict__ dlast, const float* __restrict__ ckpt, Tin* __restrict__ dxg,
-    Tin* __restrict__ ddtg, Tin* __restrict__ dzg, float* __restrict__ gBp, float* __restrict__ gCp,
-    float* __restrict__ gAp, float* __restrict__ gDp, float* __restrict__ gbp, float* __restrict__ dh0,
-    BwdShape sh) {
+    const float* __restrict__ dlast, const float* __restrict__ gin, const float* __restrict__ ckpt,
+    Tin* __restrict__ dxg, Tin* __restrict__ ddtg, Tin* __restrict__ dzg, float* __restrict__ gBp,
+    float* __restrict__ gCp, float* __restrict__ gAp, float* __restrict__ gDp, float* __restrict__ gbp,
+    float* __restrict__ dh0, BwdShape sh) {
   constexpr int T = kBwdBlock;        // timesteps per block (one checkpoint each)
   constexpr int S = kBwdSpw;          // states per wave
   constexpr int NSP = NW * S;         // states covered (N rounded up)
@@ -141,9 +141,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tid = threadIdx.x;
 
-  const int64_t blk = bwd_xcd_remap(blockIdx.x, sh.ndtiles * sh.batch);
+  int64_t blk = bwd_xcd_remap(blockIdx.x, sh.ndtiles * sh.batch * sh.nseg);
   const int64_t dtile = blk % sh.ndtiles;
-  const int64_t b = blk / sh.ndtiles;
+  blk /= sh.ndtiles;
+  const int64_t b = blk % sh.batch;
+  const int seg = static_cast<int>(blk / sh.batch);
   const int64_t L = sh.L, dim = sh.dim;
   const int N = NFIX > 0 ? NFIX : sh.N;
   const int dim32 = static_cast<int>(dim);   // T * dim < 2^31 (checked by the host)
@@ -158,6 +160,13 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(
   // this wave's states n0 .. n0 + 3; phantom states (n >= N) get A = 0 and stay
   // out of every output
   const int n0 = S * w;
+  // gradient entering the end of this segment ([batch][dim][N] slice): the carry of
+  // the sequence split, or dLoss/d(last state) for the last segment
+  const float* g_in = nullptr;
+  if (gin)
+    g_in = gin + static_cast<int64_t>(seg) * sh.batch * dim * N;
+  else if (seg == sh.nseg - 1)
+    g_in = dlast;
   float An[S], iAn[S], G[S], gA[S];
   bool anyzero = false;
 #pragma unroll
@@ -166,7 +175,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(
     An[q] = have ? Ag[dd * N + n0 + q] : 0.f;
     iAn[q] = (An[q] != 0.f) ? 1.f / An[q] : 0.f;
     anyzero = anyzero || (have && An[q] == 0.f);
-    G[q] = (dlast && have && dvalid) ? dlast[(b * dim + d) * N + n0 + q] : 0.f;
+    G[q] = (g_in && have && dvalid) ? g_in[(b * dim + d) * N + n0 + q] : 0.f;
     gA[q] = 0.f;
   }
   const bool zeroA = __any(dvalid && anyzero);
@@ -227,8 +236,10 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(
   };
 
   const int64_t nblk = sh.nblk;
-  if (nblk > 0) prologue(nblk - 1);
-  for (int64_t j = nblk - 1; j >= 0; --j) {
+  const int64_t jbeg = static_cast<int64_t>(seg) * sh.seg_blocks;
+  const int64_t jend = (jbeg + sh.seg_blocks < nblk) ? jbeg + sh.seg_blocks : nblk;
+  if (jend > jbeg) prologue(jend - 1);
+  for (int64_t j = jend - 1; j >= jbeg; --j) {
     const int pb = static_cast<int>(j & 1);
     const int64_t l0 = j * T;
     const int cnt = static_cast<int>((L - l0) < T ? (L - l0) : T);
@@ -317,11 +328,21 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(
             phi = delta;
             r2 = fmaf(gh, fmaf(An[q] * a, hp, bx), r2);
             gA[q] = fmaf(gh, delta * a * hp, gA[q]);
+          } else if (!zeroA) {
+            // d h / d A = Delta Abar (h_{l-1} + k) - phi k with k = B x / A: the term
+            // (Delta Abar - phi) k cancels for small Delta A, but only down to a few
+            // ulp of Delta Abar k, the size of the leading term Delta Abar h_{l-1}
+            phi = (a - 1.f) * iAn[q];
+            r2 = fmaf(gh * a, fmaf(An[q], hp, bx), r2);
+            const float k = bx * iAn[q];
+            gA[q] = fmaf(gh, fmaf(delta * a, hp + k, -phi * k), gA[q]);
           } else {
             phi = (An[q] != 0.f) ? (a - 1.f) * iAn[q] : delta;
             r2 = fmaf(gh * a, fmaf(An[q], hp, bx), r2);
-            // both forms are computed (each finite everywhere) and blended, so no
-            // per-lane branch splits the step
+            // a wave with some A == 0: dphi/dA = Delta^2 (u e^u - e^u + 1)/u^2, u = Delta A,
+            // from its series for |u| < 0.5 and its closed form otherwise; both are
+            // computed (each finite everywhere) and blended, so no per-lane branch
+            // splits the step
             const float u = delta * An[q];
             const float ser = delta * delta * dphi1_series(fmaxf(fminf(u, 0.5f), -0.5f));
             const float dir = (delta * a - phi) * iAn[q];
@@ -379,14 +400,15 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(
         accBias += gdt;
       }
     }
-    if (j > 0) prologue(j - 1);
+    if (j > jbeg) prologue(j - 1);
   }
 
-  // per-batch-row partial sums of dA, dD and dbias
+  // per-(segment, batch row) partial sums of dA, dD and dbias
+  const int64_t prow = static_cast<int64_t>(seg) * sh.batch + b;
   if (dvalid) {
 #pragma unroll
     for (int q = 0; q < S; ++q)
-      if (n0 + q < N) gAp[(b * N + n0 + q) * dim + d] = gA[q];
+      if (n0 + q < N) gAp[(prow * N + n0 + q) * dim + d] = gA[q];
   }
   __syncthreads();
   s_r1[w][0][lane] = accD;
@@ -399,48 +421,164 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(
       sD += s_r1[q][0][lane];
       sb += s_r2[q][0][lane];
     }
-    gDp[b * dim + d] = sD;
-    gbp[b * dim + d] = sb;
+    gDp[prow * dim + d] = sD;
+    gbp[prow * dim + d] = sb;
   }
 }
 
-// dB[b][l][n] = sum over channel tiles of the partials (fixed order), in the token dtype.
+// Reverse aggregates of the sequence split: for every segment but the last, the
+// reverse recurrence G <- Abar (gyo C + G) run over the segment from G = 0 at its end
+// gives the gradient its steps send to the state before its start (ragg_g); with the
+// segment's sum of Delta*log2(e) (ragg_s), exp2(A * sum) is the product of Abar over
+// it.  A workgroup per (batch row, channel tile, segment); one state per wave (this
+// pass needs few registers, so it takes the wide layout for occupancy), blocks of
+// kAggBlock steps staged through LDS.
+constexpr int kAggBlock = 32;
+
+template <typename Tin, int NW, int NFIX>
+__global__ __launch_bounds__(NW * 64) void bwd_agg_kernel(
+    const Tin* __restrict__ dtg, const Tin* __restrict__ zg, const Tin* __restrict__ Cg,
+    const Tin* __restrict__ dyg, const float* __restrict__ Ag, const float* __restrict__ biasg,
+    float* __restrict__ ragg_g, float* __restrict__ ragg_s, BwdShape sh) {
+  constexpr int T = kAggBlock;
+  constexpr int TPW = T / NW;
+  static_assert(T % NW == 0, "block must split evenly over waves");
+  __shared__ float s_d2[T][kTile];
+  __shared__ float s_go[T][kTile];
+  __shared__ float s_C[NW][T];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tid = threadIdx.x;
+  // segments 1 .. nseg-1 (the first segment's aggregate is never needed)
+  int64_t blk = bwd_xcd_remap(blockIdx.x, sh.ndtiles * sh.batch * (sh.nseg - 1));
+  const int64_t dtile = blk % sh.ndtiles;
+  blk /= sh.ndtiles;
+  const int64_t b = blk % sh.batch;
+  const int seg = static_cast<int>(blk / sh.batch) + 1;
+  const int64_t L = sh.L, dim = sh.dim;
+  const int N = NFIX > 0 ? NFIX : sh.N;
+  const int dim32 = static_cast<int>(dim);
+  const int64_t d = dtile * kTile + lane;
+  const bool dvalid = d < dim;
+  const int64_t dd = dvalid ? d : dim - 1;
+  const bool hasZ = zg != nullptr;
+  const float bias2 = biasg ? biasg[dd] * kLog2e : 0.f;
+  const int n = w;   // phantom states (n >= N) have A = 0, C = 0 and are not written
+  const float An = (n < N) ? Ag[dd * N + n] : 0.f;
+  float G = 0.f;
+  float ssum = 0.f, scomp = 0.f;
+
+  const int64_t l_beg = static_cast<int64_t>(seg) * sh.seg_blocks * kBwdBlock;
+  const int64_t l_end = (l_beg + sh.seg_blocks * kBwdBlock < L) ? l_beg + sh.seg_blocks * kBwdBlock : L;
+  const int64_t nb = (l_end - l_beg + T - 1) / T;
+  const int64_t tok_b = b * L * dim + dtile * kTile;
+  for (int64_t c = nb - 1; c >= 0; --c) {
+    const int64_t l0 = l_beg + c * T;
+    const int cnt = static_cast<int>((l_end - l0) < T ? (l_end - l0) : T);
+    const int64_t base = tok_b + l0 * dim;
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int t = w + NW * i;
+      float dtv = 0.f, zv = 0.f, gy = 0.f;
+      if (dvalid && t < cnt) {
+        const int off = t * dim32 + lane;
+        dtv = to_f32((dtg + base)[off]);
+        gy = to_f32((dyg + base)[off]);
+        if (hasZ) zv = to_f32((zg + base)[off]);
+      }
+      float go = gy;
+      if (hasZ) go = gy * (zv * hw_rcp(1.f + hw_exp2(-zv * kLog2e)));
+      s_d2[t][lane] = (t < cnt) ? softplus_log2e(fmaf(dtv, kLog2e, bias2)) : 0.f;
+      s_go[t][lane] = go;
+    }
+    const Tin* __restrict__ Cb = Cg + (b * L + l0) * N;
+    for (int i = tid; i < T * NW; i += NW * 64) {
+      const int nn = i / T, t = i - nn * T;
+      s_C[nn][t] = (nn < N && t < cnt) ? to_f32(Cb[t * N + nn]) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int t = T - 1; t >= 0; --t) {
+      const float d2 = s_d2[t][lane];
+      G = hw_exp2(d2 * An) * fmaf(s_go[t][lane], s_C[n][t], G);
+      if (w == 0) {   // Kahan sum of Delta*log2(e) (padded steps add 0)
+        const float yk = d2 - scomp;
+        const float tk = ssum + yk;
+        scomp = (tk - ssum) - yk;
+        ssum = tk;
+      }
+    }
+    __syncthreads();
+  }
+  if (dvalid) {
+    const int64_t row = (static_cast<int64_t>(seg) * sh.batch + b) * dim + d;
+    if (n < N) ragg_g[row * N + n] = G;
+    if (w == 0) ragg_s[row] = ssum;
+  }
+}
+
+// gin[s] = gradient entering the end of segment s: gin[nseg-1] = dLoss/d(last state)
+// (or 0), gin[s-1] = exp2(A * sum_s) * gin[s] + ragg_g[s].
+__global__ __launch_bounds__(256) void bwd_carry_kernel(const float* __restrict__ ragg_g,
+                                                        const float* __restrict__ ragg_s, const float* __restrict__ A,
+                                                        const float* __restrict__ dlast, float* __restrict__ gin,
+                                                        int64_t batch, int64_t dim, int N, int nseg) {
+  const int64_t total = batch * dim * N;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int64_t bd = i / N;
+  const int n = static_cast<int>(i - bd * N);
+  const int64_t d = bd % dim;
+  const float a = A[d * N + n];
+  float g = dlast ? dlast[i] : 0.f;
+  for (int s = nseg - 1; s >= 0; --s) {
+    gin[static_cast<int64_t>(s) * total + i] = g;
+    if (s > 0)
+      g = fmaf(hw_exp2(a * ragg_s[static_cast<int64_t>(s) * batch * dim + bd]), g,
+               ragg_g[static_cast<int64_t>(s) * total + i]);
+  }
+}
+
+// dB[b][l][n] = sum over channel tiles of the partials (fixed order), in the token
+// dtype; one thread per (b, n, l), l fastest, so the partial reads coalesce.
 template <typename Tin>
 __global__ __launch_bounds__(256) void bwd_reduce_bc(const float* __restrict__ gBp, const float* __restrict__ gCp,
                                                      Tin* __restrict__ dB, Tin* __restrict__ dC, int64_t batch,
                                                      int64_t L, int N, int64_t ndtiles) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= batch * L) return;
-  const int64_t b = i / L, l = i - b * L;
-  for (int n = 0; n < N; ++n) {
-    float sB = 0.f, sC = 0.f;
-    for (int64_t k = 0; k < ndtiles; ++k) {
-      const int64_t off = ((k * batch + b) * N + n) * L + l;
-      sB += gBp[off];
-      sC += gCp[off];
-    }
-    store_val(&dB[i * N + n], sB);
-    store_val(&dC[i * N + n], sC);
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;   // (b * N + n) * L + l
+  const int64_t per_tile = batch * N * L;
+  if (i >= per_tile) return;
+  const int64_t l = i % L;
+  const int64_t bn = i / L;
+  const int64_t n = bn % N, b = bn / N;
+  float sB = 0.f, sC = 0.f;
+  for (int64_t k = 0; k < ndtiles; ++k) {
+    sB += gBp[k * per_tile + i];
+    sC += gCp[k * per_tile + i];
   }
+  const int64_t o = (b * L + l) * N + n;
+  store_val(&dB[o], sB);
+  store_val(&dC[o], sC);
 }
 
-// dA[d][n], dD[d], dbias[d] = sums over batch rows of the partials (fixed order).
+// dA[d][n], dD[d], dbias[d] = sums over (segment, batch row) partials (fixed order).
 __global__ __launch_bounds__(256) void bwd_reduce_params(const float* __restrict__ gAp, const float* __restrict__ gDp,
                                                          const float* __restrict__ gbp, float* __restrict__ dA,
                                                          float* __restrict__ dD, float* __restrict__ dbias,
-                                                         int64_t batch, int64_t dim, int N) {
+                                                         int64_t rows, int64_t dim, int N) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= dim * N) return;
   const int64_t d = i / N;
   const int n = static_cast<int>(i - d * N);
   float s = 0.f;
-  for (int64_t b = 0; b < batch; ++b) s += gAp[(b * N + n) * dim + d];
+  for (int64_t r = 0; r < rows; ++r) s += gAp[(r * N + n) * dim + d];
   dA[i] = s;
   if (n == 0) {
     float sD = 0.f, sb = 0.f;
-    for (int64_t b = 0; b < batch; ++b) {
-      sD += gDp[b * dim + d];
-      sb += gbp[b * dim + d];
+    for (int64_t r = 0; r < rows; ++r) {
+      sD += gDp[r * dim + d];
+      sb += gbp[r * dim + d];
     }
     if (dD) dD[d] = sD;
     if (dbias) dbias[d] = sb;
@@ -451,13 +589,23 @@ namespace {
 
 template <typename Tin, int NW, int NF, bool EU>
 void launch_bwd_one(const BwdParams& p, hipStream_t s) {
-  BwdShape sh{p.batch, p.L, p.dim, p.ndtiles, p.nblk, p.N};
-  hipLaunchKernelGGL((bwd_kernel<Tin, NW, NF, EU>), dim3(static_cast<unsigned>(p.ndtiles * p.batch)),
+  BwdShape sh{p.batch, p.L, p.dim, p.ndtiles, p.nblk, p.seg_blocks, p.N, p.nseg};
+  if (p.nseg > 1) {
+    constexpr int AW = NW * kBwdSpw;   // one state per wave in the aggregate pass
+    hipLaunchKernelGGL((bwd_agg_kernel<Tin, AW, NF>), dim3(static_cast<unsigned>(p.ndtiles * p.batch * (p.nseg - 1))),
+                       dim3(AW * 64), 0, s, static_cast<const Tin*>(p.dt), static_cast<const Tin*>(p.z),
+                       static_cast<const Tin*>(p.C), static_cast<const Tin*>(p.dy), p.A, p.bias, p.ragg_g, p.ragg_s,
+                       sh);
+    const int64_t total = p.batch * p.dim * p.N;
+    hipLaunchKernelGGL(bwd_carry_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s,
+                       p.ragg_g, p.ragg_s, p.A, p.dlast, p.gin, p.batch, p.dim, p.N, p.nseg);
+  }
+  hipLaunchKernelGGL((bwd_kernel<Tin, NW, NF, EU>), dim3(static_cast<unsigned>(p.ndtiles * p.batch * p.nseg)),
                      dim3(NW * 64), 0, s, static_cast<const Tin*>(p.x), static_cast<const Tin*>(p.dt),
                      static_cast<const Tin*>(p.z), static_cast<const Tin*>(p.B), static_cast<const Tin*>(p.C),
-                     static_cast<const Tin*>(p.dy), p.A, p.Dskip, p.bias, p.dlast, p.ckpt, static_cast<Tin*>(p.dx),
-                     static_cast<Tin*>(p.ddt), static_cast<Tin*>(p.dz), p.gB_part, p.gC_part, p.gA_part,
-                     p.gD_part, p.gbias_part, p.dh0, sh);
+                     static_cast<const Tin*>(p.dy), p.A, p.Dskip, p.bias, p.dlast, p.nseg > 1 ? p.gin : nullptr,
+                     p.ckpt, static_cast<Tin*>(p.dx), static_cast<Tin*>(p.ddt), static_cast<Tin*>(p.dz), p.gB_part,
+                     p.gC_part, p.gA_part, p.gD_part, p.gbias_part, p.dh0, sh);
 }
 
 template <typename Tin, bool EU>
@@ -482,7 +630,7 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
     launch_bwd_n<Tin, false>(p, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t nbl = p.batch * p.L;
+  const int64_t nbl = p.batch * p.N * p.L;
   hipLaunchKernelGGL((bwd_reduce_bc<Tin>), dim3(static_cast<unsigned>((nbl + 255) / 256)), dim3(256), 0, s,
                      p.gB_part, p.gC_part, static_cast<Tin*>(p.dB), static_cast<Tin*>(p.dC), p.batch, p.L, p.N,
                      p.ndtiles);
@@ -490,7 +638,7 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
   if (e != hipSuccess) return e;
   const int64_t ndn = p.dim * p.N;
   hipLaunchKernelGGL(bwd_reduce_params, dim3(static_cast<unsigned>((ndn + 255) / 256)), dim3(256), 0, s, p.gA_part,
-                     p.gD_part, p.gbias_part, p.dA, p.dD, p.dbias, p.batch, p.dim, p.N);
+                     p.gD_part, p.gbias_part, p.dA, p.dD, p.dbias, p.batch * p.nseg, p.dim, p.N);
   return hipGetLastError();
 }
 

@@ -80,23 +80,29 @@ struct BwdParams {
   void* dz;               // nullable (iff z is)
   float* gB_part;         // [ndtiles][batch][N][L] per channel-tile partial sums
   float* gC_part;         // [ndtiles][batch][N][L]
-  float* gA_part;         // [batch][N][dim]
-  float* gD_part;         // [batch][dim]
-  float* gbias_part;      // [batch][dim]
+  float* gA_part;         // [nseg][batch][N][dim]
+  float* gD_part;         // [nseg][batch][dim]
+  float* gbias_part;      // [nseg][batch][dim]
   float* dh0;             // nullable: [batch][dim][N]
   void* dB;               // [batch][L][N] (token dtype)
   void* dC;
   float* dA;              // [dim][N]
   float* dD;              // nullable
   float* dbias;           // nullable
+  // sequence split of the reverse pass (nseg > 1): per-segment aggregates and carries
+  float* ragg_g;          // [nseg][batch][dim][N] gradient leaving each segment's start from a zero end
+  float* ragg_s;          // [nseg][batch][dim]    sum of Delta*log2(e) over each segment
+  float* gin;             // [nseg][batch][dim][N] gradient entering each segment's end
   int64_t batch, L, dim, ndtiles, nblk;
+  int64_t seg_blocks;     // blocks of kBwdBlock steps per segment
   int N;
+  int nseg;
   bool euler;
 };
 
 struct BwdShape {
-  int64_t batch, L, dim, ndtiles, nblk;
-  int N;
+  int64_t batch, L, dim, ndtiles, nblk, seg_blocks;
+  int N, nseg;
 };
 
 hipError_t launch_bwd(const BwdParams& p, bool bf16, hipStream_t s);
