@@ -23,6 +23,11 @@ What it computes, and the passages it follows (the reference pages):
 * Recurrent step on a carried (B, D, N) state: page-3 report section 6 (ssm_step).
 * ``euler=True``: Bbar = Delta B, the first-order rule of the page-3 report's code
   (section 4.2, ``deltaB = delta * B``).
+* ``conv_silu_prologue``: the short causal depthwise convolution over time and the
+  SiLU that precede the scan in the page-3 report's MambaBlock (section 3,
+  ``forward``: conv1d with kernel d_conv and padding d_conv - 1, cropped to the
+  first L outputs, then silu), with the convolution cache of its ``step``
+  (section 6: the last d_conv - 1 raw inputs, oldest first).
 * ``sscan_bwd``: gradients of a scalar loss with respect to every input, by the
   chain rule through the definition above, run backwards in time (the reverse
   recurrence that the page-3 report's ``pscan_rev`` serves, section 4.1).
@@ -191,6 +196,36 @@ class Oracle:
             raise ValueError("oracle_sscan_bwd rejected its arguments")
         self.last_threads_used = used
         return out
+
+
+def conv_silu_prologue(x, w, conv_bias=None, conv_state=None):
+    """fp64 causal depthwise convolution over time followed by SiLU.
+
+    x: [batch, seqlen, dim] raw inputs; w: [dim, dconv] filter taps (w[:, dconv-1]
+    multiplies the current input, w[:, 0] the oldest); conv_bias: [dim] or None;
+    conv_state: [batch, dim, dconv-1] raw inputs before x (oldest first), zeros if
+    None.  Returns (u [batch, seqlen, dim], new_state [batch, dim, dconv-1]):
+        c[b,l,d] = sum_k w[d,k] * xx[b, l + k, d] + conv_bias[d]
+    where xx is x preceded along time by conv_state, and u = c * sigmoid(c); the new
+    state is the last dconv - 1 entries of xx.  (Page-3 report, sections 3 and 6.)
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    Bt, L, Dm = x.shape
+    K = w.shape[1]
+    if w.shape[0] != Dm or K < 1:
+        raise ValueError("w must be [dim, dconv]")
+    st = (np.zeros((Bt, Dm, K - 1)) if conv_state is None
+          else np.asarray(conv_state, dtype=np.float64).reshape(Bt, Dm, K - 1))
+    xx = np.concatenate([np.transpose(st, (0, 2, 1)), x], axis=1)      # [batch, K-1+L, dim]
+    c = np.zeros((Bt, L, Dm))
+    for k in range(K):
+        c += w[None, None, :, k] * xx[:, k:k + L, :]
+    if conv_bias is not None:
+        c += np.asarray(conv_bias, dtype=np.float64)[None, None, :]
+    u = c / (1.0 + np.exp(-c))
+    new_state = np.transpose(xx[:, L:, :], (0, 2, 1)).copy() if K > 1 else np.zeros((Bt, Dm, 0))
+    return u, new_state
 
 
 _default: Optional[Oracle] = None
