@@ -35,7 +35,7 @@ OPS_PER_STATE_UPDATE = 8     # Delta*A, exp (2), B/A scale, x scale, add, fma (s
 OPS_PER_TOKEN_CHANNEL = 20   # softplus 11, silu 7, skip + gate 2
 PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "sscan_fwd_train_shape_counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_45_amd", "csrc", f)
-                  for f in ("sscan_fwd.hip", "sscan_device.h", "sscan_internal.h")]
+                  for f in ("sscan_fwd_kernel.h", "sscan_fwd_zoh.hip", "sscan_device.h", "sscan_internal.h")]
 
 
 def kernel_source_hash() -> str:

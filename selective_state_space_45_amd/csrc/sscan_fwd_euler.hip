@@ -1,0 +1,10 @@
+// Forward scan launch variants: Euler rule (Bbar = Delta B).
+#include "sscan_fwd_kernel.h"
+
+namespace sscan {
+
+template hipError_t launch_fwd_variant<kFwdOut, true>(const FwdParams&, bool, hipStream_t);
+template hipError_t launch_fwd_variant<kFwdAgg, true>(const FwdParams&, bool, hipStream_t);
+template hipError_t launch_fwd_variant<kFwdCkpt, true>(const FwdParams&, bool, hipStream_t);
+
+}  // namespace sscan

@@ -1,0 +1,10 @@
+// Forward scan launch variants: zero-order hold.
+#include "sscan_fwd_kernel.h"
+
+namespace sscan {
+
+template hipError_t launch_fwd_variant<kFwdOut, false>(const FwdParams&, bool, hipStream_t);
+template hipError_t launch_fwd_variant<kFwdAgg, false>(const FwdParams&, bool, hipStream_t);
+template hipError_t launch_fwd_variant<kFwdCkpt, false>(const FwdParams&, bool, hipStream_t);
+
+}  // namespace sscan
