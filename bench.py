@@ -7,7 +7,7 @@ bf16 x/delta/z/B/C/y, fp32 A/D/bias/state.  Inputs are resident in HBM before th
 timed region.  One JSON line is printed.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
-                    [--no-euler] [--no-bwd] [--copy-calibration]
+                    [--no-euler] [--no-bwd] [--no-conv] [--copy-calibration]
     python bench.py --summarize-counters FETCH_CSV WRITE_CSV   (CPU only)
 
 --copy-calibration also runs a plain 512 MiB -> 512 MiB elementwise copy (three
@@ -120,6 +120,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step leg")
     ap.add_argument("--no-euler", action="store_true", help="skip the Euler-rule leg")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward-pass leg")
+    ap.add_argument("--no-conv", action="store_true", help="skip the convolution-prologue leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 512 MiB elementwise copy (counter calibration)")
     ap.add_argument("--decode-steps", type=int, default=100)
@@ -196,6 +197,28 @@ def main():
         euler = {"op": "sscan_fwd, Euler rule (flag SSCAN_FLAG_EULER)", "kernel_ms": round(eu_ms, 5),
                  "gbs": round(nbytes / (eu_ms * 1e-3) / 1e9, 2),
                  "hbm_frac_of_peak": round(nbytes / (eu_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+    # the fused convolution prologue (causal depthwise conv1d, 4 taps, + SiLU) on the
+    # same workload: x is then the convolution's raw input
+    conv = None
+    if not args.no_conv:
+        K = 4
+        cw = torch.randn(w.dim, K, device=dev) * 0.5
+        cb = torch.randn(w.dim, device=dev) * 0.1
+        cs_in = torch.randn(w.batch, w.dim, K - 1, device=dev)
+        cs_out = torch.empty_like(cs_in)
+
+        def step_conv():
+            ss.sscan_fwd(x, dt, A, B, C, D=D, z=z, delta_bias=bias, out=y, last_state=st, workspace=ws,
+                         conv_w=cw, conv_b=cb, conv_state_in=cs_in, conv_state_out=cs_out)
+
+        for _ in range(3):
+            step_conv()
+        torch.cuda.synchronize()
+        cv_ms = timed_launches(step_conv, max(5, args.steps // 2))
+        cv_bytes = nbytes + 4 * w.dim * (K + 1) + 2 * 4 * w.batch * w.dim * (K - 1)
+        conv = {"op": "sscan_fwd_conv (fused causal conv1d, 4 taps, + SiLU prologue)", "ms": round(cv_ms, 5),
+                "algorithmic_bytes": cv_bytes, "gbs": round(cv_bytes / (cv_ms * 1e-3) / 1e9, 2)}
 
     # backward pass (sscan_bwd: checkpoint pass, reverse pass, reductions) on the same
     # workload, reported alongside
@@ -306,6 +329,7 @@ def main():
                      "kernel_ms": round(kern_ms, 5), "kernel_gbs": round(kern_gbs, 2),
                      "algorithmic_bytes": nbytes, "algorithmic_ops": ops},
         "euler": euler,
+        "conv": conv,
         "bwd": bwd,
         "decode": decode,
         "cpu_baseline": cpu,

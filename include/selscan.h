@@ -49,8 +49,9 @@
 extern "C" {
 #endif
 
-#define SSCAN_VERSION 300
+#define SSCAN_VERSION 400
 #define SSCAN_MAX_DSTATE 16
+#define SSCAN_MAX_DCONV 4
 
 /*
  * Bits of the `flags` argument.
@@ -144,6 +145,53 @@ int sscan_step(int64_t batch, int64_t dim, int64_t dstate, int dtype, unsigned i
                float* state, const void* x, const void* delta, const float* A,
                const void* B, const void* C, const float* D, const void* z,
                const float* delta_bias, void* y, void* stream);
+
+/*
+ * sscan_fwd with the short convolution that precedes the scan in a Mamba block,
+ * fused into the scan's load: the page-3 report's MambaBlock.forward
+ * (Mamba_Model_Report.md, section 3) passes the x branch through a causal depthwise
+ * conv1d over time (kernel d_conv, padding d_conv - 1, output cropped to the first
+ * L steps) and a SiLU before the selective scan:
+ *   u[b,l,d] = silu(conv_b[d] + sum_{k<dconv} conv_w[d,k] * xx[b, l - (dconv-1) + k, d])
+ * where xx is x preceded along time by conv_state_in (the dconv - 1 raw inputs
+ * before the sequence, oldest first; zeros when NULL).  The scan, skip term and gate
+ * then use u in place of x.  conv_state_out receives the last dconv - 1 raw inputs
+ * (the cache that MambaBlock.step keeps, section 6), so a prefill hands over to
+ * sscan_step_conv.
+ *
+ *   x              : [batch, seqlen, dim]    (dtype) raw inputs of the convolution
+ *   conv_w         : [dim, dconv]            (float32) taps, conv_w[:, dconv-1] on the current input
+ *   conv_b         : [dim]                   (float32) or NULL
+ *   conv_state_in  : [batch, dim, dconv - 1] (float32) or NULL
+ *   conv_state_out : [batch, dim, dconv - 1] (float32) or NULL; may be conv_state_in
+ *   other arguments: as sscan_fwd.
+ * 1 <= dconv <= SSCAN_MAX_DCONV (else SSCAN_ERR_UNSUPPORTED).  The backward pass does
+ * not include the convolution: sscan_bwd differentiates the scan with respect to u.
+ */
+int sscan_fwd_conv(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int64_t dconv,
+                   int dtype, unsigned int flags, const void* x, const float* conv_w,
+                   const float* conv_b, const float* conv_state_in, float* conv_state_out,
+                   const void* delta, const float* A, const void* B, const void* C,
+                   const float* D, const void* z, const float* delta_bias,
+                   const float* initial_state, void* y, float* last_state, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/*
+ * sscan_step with the convolution prologue: the page-3 report's MambaBlock.step
+ * (section 6) convolves the cached dconv - 1 raw inputs and the new one, applies
+ * SiLU, runs the SSM step on the result, and updates the cache by dropping its
+ * oldest entry and appending the new raw input.
+ *
+ *   conv_state : [batch, dim, dconv - 1] (float32) read, then updated in place
+ *                (may be NULL only when dconv == 1)
+ *   x          : [batch, dim] (dtype) raw input
+ *   conv_w, conv_b, dconv: as sscan_fwd_conv; other arguments: as sscan_step.
+ */
+int sscan_step_conv(int64_t batch, int64_t dim, int64_t dstate, int64_t dconv, int dtype,
+                    unsigned int flags, float* state, float* conv_state, const void* x,
+                    const float* conv_w, const float* conv_b, const void* delta, const float* A,
+                    const void* B, const void* C, const float* D, const void* z,
+                    const float* delta_bias, void* y, void* stream);
 
 /*
  * Workspace bytes sscan_bwd needs for a shape (0 for an empty problem).  The

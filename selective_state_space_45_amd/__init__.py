@@ -39,6 +39,10 @@ _lib.sscan_fwd_segmented.argtypes = [_I64, _I64, _I64, _I64, ctypes.c_int, _U32]
 _lib.sscan_fwd_segmented.restype = ctypes.c_int
 _lib.sscan_step.argtypes = [_I64, _I64, _I64, ctypes.c_int, _U32] + [_P] * 11
 _lib.sscan_step.restype = ctypes.c_int
+_lib.sscan_fwd_conv.argtypes = [_I64, _I64, _I64, _I64, _I64, ctypes.c_int, _U32] + [_P] * 15 + [_P, _SZ, _P]
+_lib.sscan_fwd_conv.restype = ctypes.c_int
+_lib.sscan_step_conv.argtypes = [_I64, _I64, _I64, _I64, ctypes.c_int, _U32] + [_P] * 14
+_lib.sscan_step_conv.restype = ctypes.c_int
 _lib.sscan_bwd_workspace_size.argtypes = [_I64, _I64, _I64, _I64, ctypes.c_int]
 _lib.sscan_bwd_workspace_size.restype = _SZ
 _lib.sscan_bwd.argtypes = [_I64, _I64, _I64, _I64, ctypes.c_int, _U32] + [_P] * 21 + [_SZ, _P]
@@ -103,11 +107,15 @@ def sscan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Te
               delta_bias: Optional[torch.Tensor] = None, initial_state: Optional[torch.Tensor] = None,
               return_last_state: bool = False, out: Optional[torch.Tensor] = None,
               last_state: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-              num_segments: Optional[int] = None, euler: bool = False):
+              num_segments: Optional[int] = None, euler: bool = False,
+              conv_w: Optional[torch.Tensor] = None, conv_b: Optional[torch.Tensor] = None,
+              conv_state_in: Optional[torch.Tensor] = None, conv_state_out: Optional[torch.Tensor] = None):
     """Forward selective scan.  x, delta, z: [batch, seqlen, dim]; B, C: [batch, seqlen, dstate]
     (all float32 or all bfloat16); A: [dim, dstate], D, delta_bias: [dim], initial_state:
     [batch, dim, dstate] (float32).  euler: Bbar = Delta B instead of the zero-order hold.
-    Returns y, or (y, last_state)."""
+    conv_w [dim, dconv] (float32): x is the raw input of the fused causal depthwise
+    convolution + SiLU prologue (conv_b [dim], conv_state_in / conv_state_out
+    [batch, dim, dconv - 1], float32, optional).  Returns y, or (y, last_state)."""
     if x.dim() != 3:
         raise ValueError("x must be [batch, seqlen, dim]")
     batch, seqlen, dim = x.shape
@@ -144,7 +152,20 @@ def sscan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Te
     flags = SSCAN_FLAG_EULER if euler else 0
     args = [batch, seqlen, dim, dstate, dt, flags, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
             _ptr(delta_bias), _ptr(initial_state), _ptr(y), _ptr(ls), _ptr(workspace), wbytes]
-    if num_segments is None:
+    if conv_w is not None:
+        if num_segments is not None:
+            raise ValueError("num_segments is not available with the convolution prologue")
+        dconv = conv_w.shape[1] if conv_w.dim() == 2 else -1
+        _dev(conv_w, "conv_w", torch.float32, (dim, dconv))
+        if conv_b is not None:
+            _dev(conv_b, "conv_b", torch.float32, (dim,))
+        for t, name in ((conv_state_in, "conv_state_in"), (conv_state_out, "conv_state_out")):
+            if t is not None:
+                _dev(t, name, torch.float32, (batch, dim, dconv - 1))
+        cargs = [batch, seqlen, dim, dstate, dconv, dt, flags, _ptr(x), _ptr(conv_w), _ptr(conv_b),
+                 _ptr(conv_state_in), _ptr(conv_state_out)] + args[7:]
+        _check(_lib.sscan_fwd_conv(*cargs, _stream(x.device)))
+    elif num_segments is None:
         _check(_lib.sscan_fwd(*args, _stream(x.device)))
     else:
         _check(_lib.sscan_fwd_segmented(*args, int(num_segments), _stream(x.device)))
@@ -156,10 +177,13 @@ def sscan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Te
 def sscan_step(state: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
                C: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
                delta_bias: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-               euler: bool = False) -> torch.Tensor:
+               euler: bool = False, conv_w: Optional[torch.Tensor] = None, conv_b: Optional[torch.Tensor] = None,
+               conv_state: Optional[torch.Tensor] = None) -> torch.Tensor:
     """One decode step.  state: [batch, dim, dstate] float32, updated in place; x, delta, z:
     [batch, dim]; B, C: [batch, dstate] (float32 or bfloat16); A: [dim, dstate].  euler: Bbar =
-    Delta B instead of the zero-order hold.  Returns y [batch, dim]."""
+    Delta B instead of the zero-order hold.  conv_w [dim, dconv]: x is a raw input of the
+    convolution prologue whose cache conv_state [batch, dim, dconv - 1] (float32) is
+    updated in place.  Returns y [batch, dim]."""
     if x.dim() != 2:
         raise ValueError("x must be [batch, dim]")
     batch, dim = x.shape
@@ -180,8 +204,22 @@ def sscan_step(state: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, A: tor
         _dev(delta_bias, "delta_bias", torch.float32, (dim,))
     y = out if out is not None else torch.empty_like(x)
     _dev(y, "out", x.dtype, x.shape)
-    _check(_lib.sscan_step(batch, dim, dstate, _DTYPES[x.dtype], SSCAN_FLAG_EULER if euler else 0, _ptr(state), _ptr(x), _ptr(delta), _ptr(A),
-                           _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(y), _stream(x.device)))
+    flags = SSCAN_FLAG_EULER if euler else 0
+    if conv_w is not None:
+        dconv = conv_w.shape[1] if conv_w.dim() == 2 else -1
+        _dev(conv_w, "conv_w", torch.float32, (dim, dconv))
+        if conv_b is not None:
+            _dev(conv_b, "conv_b", torch.float32, (dim,))
+        if conv_state is not None:
+            _dev(conv_state, "conv_state", torch.float32, (batch, dim, dconv - 1))
+        _check(_lib.sscan_step_conv(batch, dim, dstate, dconv, _DTYPES[x.dtype], flags, _ptr(state),
+                                    _ptr(conv_state), _ptr(x), _ptr(conv_w), _ptr(conv_b), _ptr(delta), _ptr(A),
+                                    _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(y),
+                                    _stream(x.device)))
+        return y
+    _check(_lib.sscan_step(batch, dim, dstate, _DTYPES[x.dtype], flags, _ptr(state), _ptr(x), _ptr(delta),
+                           _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(y),
+                           _stream(x.device)))
     return y
 
 

@@ -101,6 +101,11 @@ bool overlaps(const void* a, size_t abytes, const void* b, size_t bbytes) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+struct Buf {
+  const void* p;
+  size_t n;
+};
+
 int check_common(int64_t batch, int64_t dim, int64_t dstate, int dtype, unsigned flags) {
   if (dtype != SSCAN_F32 && dtype != SSCAN_BF16) return fail(SSCAN_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
   if (flags & ~SSCAN_FLAG_EULER) return fail(SSCAN_ERR_UNSUPPORTED, "unknown flag bits 0x%x", flags);
@@ -111,11 +116,35 @@ int check_common(int64_t batch, int64_t dim, int64_t dstate, int dtype, unsigned
   return SSCAN_OK;
 }
 
+// Convolution prologue arguments (all null / 0 for the plain scan).
+struct ConvArgs {
+  int64_t dconv;
+  const float* w;
+  const float* b;
+  const float* state_in;
+  float* state_out;
+};
+
+int check_conv(const ConvArgs& cv, int64_t batch, int64_t dim) {
+  if (!cv.w) return SSCAN_OK;
+  if (cv.dconv < 1 || cv.dconv > sscan::kMaxConv)
+    return fail(SSCAN_ERR_UNSUPPORTED, "dconv %lld outside [1, %d]", (long long)cv.dconv, sscan::kMaxConv);
+  if (!aligned(cv.w, 4) || (cv.b && !aligned(cv.b, 4)) || (cv.state_in && !aligned(cv.state_in, 4)) ||
+      (cv.state_out && !aligned(cv.state_out, 4)))
+    return fail(SSCAN_ERR_INVALID_ARG, "float32 tensor not 4-byte aligned");
+  const size_t cs = static_cast<size_t>(batch) * dim * (cv.dconv - 1) * 4;
+  if (cv.state_in && cv.state_out && cv.state_in != cv.state_out && overlaps(cv.state_in, cs, cv.state_out, cs))
+    return fail(SSCAN_ERR_INVALID_ARG, "conv_state_in and conv_state_out partially overlap");
+  return SSCAN_OK;
+}
+
 int fwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype, unsigned flags, const void* x,
              const void* delta, const float* A, const void* B, const void* C, const float* D, const void* z,
              const float* delta_bias, const float* initial_state, void* y, float* last_state, void* workspace,
-             size_t workspace_bytes, int64_t num_segments, void* stream) {
+             size_t workspace_bytes, int64_t num_segments, void* stream, const ConvArgs& cv) {
   int rc = check_common(batch, dim, dstate, dtype, flags);
+  if (rc) return rc;
+  rc = check_conv(cv, batch, dim);
   if (rc) return rc;
   if (seqlen < 0) return fail(SSCAN_ERR_INVALID_ARG, "negative seqlen %lld", (long long)seqlen);
   if (num_segments < 0) return fail(SSCAN_ERR_INVALID_ARG, "negative num_segments");
@@ -129,8 +158,14 @@ int fwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dty
   const size_t bc = static_cast<size_t>(batch) * seqlen * N * es;
   const size_t st = static_cast<size_t>(batch) * dim * N * sizeof(float);
   if (batch == 0 || dim == 0) return ok();
+  const size_t conv_bytes = cv.w ? static_cast<size_t>(batch) * dim * (cv.dconv - 1) * 4 : 0;
 
   if (seqlen == 0) {
+    if (cv.w && cv.state_out && cv.state_out != cv.state_in) {
+      hipError_t e = sscan::launch_conv_state(x, cv.state_in, cv.state_out, batch, 0, dim, static_cast<int>(cv.dconv),
+                                              dtype == SSCAN_BF16, s);
+      if (e != hipSuccess) return hip_fail(e, "conv state launch");
+    }
     if (last_state) {
       if (initial_state && !aligned(initial_state, 4)) return fail(SSCAN_ERR_INVALID_ARG, "initial_state misaligned");
       if (!aligned(last_state, 4)) return fail(SSCAN_ERR_INVALID_ARG, "last_state misaligned");
@@ -163,6 +198,12 @@ int fwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dty
     if (initial_state && initial_state != last_state && overlaps(initial_state, st, last_state, st))
       return fail(SSCAN_ERR_INVALID_ARG, "initial_state and last_state partially overlap");
   }
+  if (cv.state_out) {
+    const Buf others[] = {{x, tok}, {delta, tok}, {z, tok}, {y, tok}, {B, bc}, {C, bc}, {last_state, st},
+                          {initial_state, st}, {cv.w, static_cast<size_t>(dim) * cv.dconv * 4}};
+    for (const Buf& o : others)
+      if (overlaps(cv.state_out, conv_bytes, o.p, o.n)) return fail(SSCAN_ERR_INVALID_ARG, "conv_state_out overlaps a tensor");
+  }
 
   const SegPlan pl = plan_segments(batch, seqlen, dim, N, num_segments, workspace_bytes, workspace != nullptr);
   if (pl.nseg > 1 && overlaps(workspace, seg_workspace_bytes(batch, dim, N, pl.nseg), y, tok))
@@ -176,13 +217,23 @@ int fwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dty
   p.ndtiles = (dim + sscan::kTile - 1) / sscan::kTile;
   p.seg_len = pl.seg_len; p.nseg = pl.nseg;
   p.euler = (flags & SSCAN_FLAG_EULER) != 0;
+  p.conv_w = cv.w; p.conv_b = cv.b; p.conv_s = cv.state_in; p.dconv = static_cast<int>(cv.w ? cv.dconv : 0);
   const bool bf16 = dtype == SSCAN_BF16;
+  // the convolution state leaves after the scan (which reads the incoming one)
+  auto finish = [&]() -> int {
+    if (cv.w && cv.state_out) {
+      hipError_t e = sscan::launch_conv_state(x, cv.state_in, cv.state_out, batch, seqlen, dim,
+                                              static_cast<int>(cv.dconv), bf16, s);
+      if (e != hipSuccess) return hip_fail(e, "conv state launch");
+    }
+    return ok();
+  };
 
   if (pl.nseg == 1) {
     p.h_init = initial_state;
     hipError_t e = sscan::launch_fwd_main(p, bf16, s);
     if (e != hipSuccess) return hip_fail(e, "scan launch");
-    return ok();
+    return finish();
   }
 
   const int64_t bdn = batch * dim * N;
@@ -199,7 +250,7 @@ int fwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dty
   p.h_init = carry;
   e = sscan::launch_fwd_main(p, bf16, s);
   if (e != hipSuccess) return hip_fail(e, "scan launch");
-  return ok();
+  return finish();
 }
 
 
@@ -306,7 +357,6 @@ int bwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dty
   const size_t tok = static_cast<size_t>(batch) * seqlen * dim * es;
   const size_t bc = static_cast<size_t>(batch) * seqlen * N * es;
   const size_t st = static_cast<size_t>(batch) * dim * N * 4;
-  struct Buf { const void* p; size_t n; };
   const Buf inputs[] = {{x, tok}, {delta, tok}, {z, tok}, {dy, tok}, {B, bc}, {C, bc}, {A, size_t(dim) * N * 4},
                         {D, size_t(dim) * 4}, {delta_bias, size_t(dim) * 4}, {initial_state, st},
                         {dlast_state, st}};
@@ -381,44 +431,17 @@ int bwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dty
   return ok();
 }
 
-}  // namespace
-
-extern "C" {
-
-int sscan_version(void) { return SSCAN_VERSION; }
-
-const char* sscan_last_error(void) { return g_last_error.c_str(); }
-
-size_t sscan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype) {
-  (void)dtype;
-  if (batch <= 0 || seqlen <= 0 || dim <= 0 || dstate < 1 || dstate > SSCAN_MAX_DSTATE) return 0;
-  const SegPlan pl = plan_segments(batch, seqlen, dim, dstate, 0, ~size_t(0), true);
-  return seg_workspace_bytes(batch, dim, dstate, pl.nseg);
-}
-
-int sscan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype, unsigned int flags,
-              const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
-              const void* z, const float* delta_bias, const float* initial_state, void* y, float* last_state,
-              void* workspace, size_t workspace_bytes, void* stream) {
-  return fwd_impl(batch, seqlen, dim, dstate, dtype, flags, x, delta, A, B, C, D, z, delta_bias, initial_state, y,
-                  last_state, workspace, workspace_bytes, 0, stream);
-}
-
-int sscan_fwd_segmented(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
-                        unsigned int flags, const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
-                        const void* z, const float* delta_bias, const float* initial_state, void* y,
-                        float* last_state, void* workspace, size_t workspace_bytes, int64_t num_segments,
-                        void* stream) {
-  return fwd_impl(batch, seqlen, dim, dstate, dtype, flags, x, delta, A, B, C, D, z, delta_bias, initial_state, y,
-                  last_state, workspace, workspace_bytes, num_segments, stream);
-}
-
-int sscan_step(int64_t batch, int64_t dim, int64_t dstate, int dtype, unsigned int flags, float* state,
-               const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
-               const void* z, const float* delta_bias, void* y, void* stream) {
+int step_impl(int64_t batch, int64_t dim, int64_t dstate, int dtype, unsigned flags, float* state, const void* x,
+              const void* delta, const float* A, const void* B, const void* C, const float* D, const void* z,
+              const float* delta_bias, void* y, void* stream, int64_t dconv, const float* conv_w,
+              const float* conv_b, float* conv_state) {
   int rc = check_common(batch, dim, dstate, dtype, flags);
   if (rc) return rc;
+  rc = check_conv(ConvArgs{dconv, conv_w, conv_b, conv_state, conv_state}, batch, dim);
+  if (rc) return rc;
   if (batch == 0 || dim == 0) return ok();
+  if (conv_w && dconv > 1 && !conv_state)
+    return fail(SSCAN_ERR_INVALID_ARG, "null required pointer (conv_state, dconv > 1)");
   if (!state || !x || !delta || !A || !B || !C || !y)
     return fail(SSCAN_ERR_INVALID_ARG, "null required pointer (state, x, delta, A, B, C and y are required)");
   const size_t es = dtype == SSCAN_BF16 ? 2 : 4;
@@ -441,9 +464,75 @@ int sscan_step(int64_t batch, int64_t dim, int64_t dstate, int dtype, unsigned i
   p.A = A; p.Dskip = D; p.bias = delta_bias; p.y = y;
   p.batch = batch; p.dim = dim; p.N = static_cast<int>(dstate);
   p.euler = (flags & SSCAN_FLAG_EULER) != 0;
+  p.conv_w = conv_w; p.conv_b = conv_b; p.conv_state = conv_state; p.dconv = static_cast<int>(conv_w ? dconv : 1);
+  if (conv_state) {
+    const size_t cs = static_cast<size_t>(batch) * dim * (dconv - 1) * 4;
+    if (overlaps(conv_state, cs, state, st) || overlaps(conv_state, cs, x, tok) || overlaps(conv_state, cs, y, tok))
+      return fail(SSCAN_ERR_INVALID_ARG, "conv_state overlaps a tensor");
+  }
   hipError_t e = sscan::launch_step(p, dtype == SSCAN_BF16, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "step launch");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int sscan_version(void) { return SSCAN_VERSION; }
+
+const char* sscan_last_error(void) { return g_last_error.c_str(); }
+
+size_t sscan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype) {
+  (void)dtype;
+  if (batch <= 0 || seqlen <= 0 || dim <= 0 || dstate < 1 || dstate > SSCAN_MAX_DSTATE) return 0;
+  const SegPlan pl = plan_segments(batch, seqlen, dim, dstate, 0, ~size_t(0), true);
+  return seg_workspace_bytes(batch, dim, dstate, pl.nseg);
+}
+
+int sscan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype, unsigned int flags,
+              const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
+              const void* z, const float* delta_bias, const float* initial_state, void* y, float* last_state,
+              void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_impl(batch, seqlen, dim, dstate, dtype, flags, x, delta, A, B, C, D, z, delta_bias, initial_state, y,
+                  last_state, workspace, workspace_bytes, 0, stream, ConvArgs{});
+}
+
+int sscan_fwd_conv(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int64_t dconv, int dtype,
+                   unsigned int flags, const void* x, const float* conv_w, const float* conv_b,
+                   const float* conv_state_in, float* conv_state_out, const void* delta, const float* A,
+                   const void* B, const void* C, const float* D, const void* z, const float* delta_bias,
+                   const float* initial_state, void* y, float* last_state, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  if (!conv_w) return fail(SSCAN_ERR_INVALID_ARG, "null required pointer (conv_w)");
+  return fwd_impl(batch, seqlen, dim, dstate, dtype, flags, x, delta, A, B, C, D, z, delta_bias, initial_state, y,
+                  last_state, workspace, workspace_bytes, 0, stream,
+                  ConvArgs{dconv, conv_w, conv_b, conv_state_in, conv_state_out});
+}
+
+int sscan_fwd_segmented(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+                        unsigned int flags, const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
+                        const void* z, const float* delta_bias, const float* initial_state, void* y,
+                        float* last_state, void* workspace, size_t workspace_bytes, int64_t num_segments,
+                        void* stream) {
+  return fwd_impl(batch, seqlen, dim, dstate, dtype, flags, x, delta, A, B, C, D, z, delta_bias, initial_state, y,
+                  last_state, workspace, workspace_bytes, num_segments, stream, ConvArgs{});
+}
+
+int sscan_step(int64_t batch, int64_t dim, int64_t dstate, int dtype, unsigned int flags, float* state,
+               const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
+               const void* z, const float* delta_bias, void* y, void* stream) {
+  return step_impl(batch, dim, dstate, dtype, flags, state, x, delta, A, B, C, D, z, delta_bias, y, stream, 0, nullptr,
+                   nullptr, nullptr);
+}
+
+int sscan_step_conv(int64_t batch, int64_t dim, int64_t dstate, int64_t dconv, int dtype, unsigned int flags,
+                    float* state, float* conv_state, const void* x, const float* conv_w, const float* conv_b,
+                    const void* delta, const float* A, const void* B, const void* C, const float* D, const void* z,
+                    const float* delta_bias, void* y, void* stream) {
+  if (!conv_w) return fail(SSCAN_ERR_INVALID_ARG, "null required pointer (conv_w)");
+  return step_impl(batch, dim, dstate, dtype, flags, state, x, delta, A, B, C, D, z, delta_bias, y, stream, dconv,
+                   conv_w, conv_b, conv_state);
 }
 
 size_t sscan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype) {

@@ -5,12 +5,16 @@
 
 namespace sscan {
 
-extern template hipError_t launch_fwd_variant<kFwdOut, false>(const FwdParams&, bool, hipStream_t);
-extern template hipError_t launch_fwd_variant<kFwdAgg, false>(const FwdParams&, bool, hipStream_t);
-extern template hipError_t launch_fwd_variant<kFwdCkpt, false>(const FwdParams&, bool, hipStream_t);
-extern template hipError_t launch_fwd_variant<kFwdOut, true>(const FwdParams&, bool, hipStream_t);
-extern template hipError_t launch_fwd_variant<kFwdAgg, true>(const FwdParams&, bool, hipStream_t);
-extern template hipError_t launch_fwd_variant<kFwdCkpt, true>(const FwdParams&, bool, hipStream_t);
+extern template hipError_t launch_fwd_variant<kFwdOut, false, false>(const FwdParams&, bool, hipStream_t);
+extern template hipError_t launch_fwd_variant<kFwdAgg, false, false>(const FwdParams&, bool, hipStream_t);
+extern template hipError_t launch_fwd_variant<kFwdCkpt, false, false>(const FwdParams&, bool, hipStream_t);
+extern template hipError_t launch_fwd_variant<kFwdOut, true, false>(const FwdParams&, bool, hipStream_t);
+extern template hipError_t launch_fwd_variant<kFwdAgg, true, false>(const FwdParams&, bool, hipStream_t);
+extern template hipError_t launch_fwd_variant<kFwdCkpt, true, false>(const FwdParams&, bool, hipStream_t);
+extern template hipError_t launch_fwd_variant<kFwdOut, false, true>(const FwdParams&, bool, hipStream_t);
+extern template hipError_t launch_fwd_variant<kFwdAgg, false, true>(const FwdParams&, bool, hipStream_t);
+extern template hipError_t launch_fwd_variant<kFwdOut, true, true>(const FwdParams&, bool, hipStream_t);
+extern template hipError_t launch_fwd_variant<kFwdAgg, true, true>(const FwdParams&, bool, hipStream_t);
 
 // carry[s] = state entering segment s: carry[0] = h_init (or 0),
 // carry[s+1] = exp2(A * S_s) * carry[s] + hend_s, where S_s is the segment's sum of
@@ -52,7 +56,39 @@ namespace {
 
 template <int MODE>
 hipError_t launch_fwd_mode(const FwdParams& p, bool bf16, hipStream_t s) {
-  return p.euler ? launch_fwd_variant<MODE, true>(p, bf16, s) : launch_fwd_variant<MODE, false>(p, bf16, s);
+  if constexpr (MODE != kFwdCkpt) {
+    if (p.conv_w)
+      return p.euler ? launch_fwd_variant<MODE, true, true>(p, bf16, s)
+                     : launch_fwd_variant<MODE, false, true>(p, bf16, s);
+  }
+  return p.euler ? launch_fwd_variant<MODE, true, false>(p, bf16, s) : launch_fwd_variant<MODE, false, false>(p, bf16, s);
+}
+
+// out[b][d][k] = raw input at position L - (dconv-1) + k (from x, or from the incoming
+// state for positions below 0).  One thread per (b, d): all reads before any write,
+// so out may be the same buffer as in.
+template <typename Tin>
+__global__ __launch_bounds__(256) void conv_state_kernel(const Tin* __restrict__ x, const float* in, float* out,
+                                                         int64_t batch, int64_t L, int64_t dim, int dconv) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= batch * dim) return;
+  const int64_t b = i / dim, d = i - b * dim;
+  const int km = dconv - 1;
+  float v[kMaxConv];
+#pragma unroll
+  for (int k = 0; k < kMaxConv - 1; ++k) {
+    v[k] = 0.f;
+    if (k < km) {
+      const int64_t pos = L - km + k;
+      if (pos >= 0)
+        v[k] = to_f32(x[(b * L + pos) * dim + d]);
+      else if (in)
+        v[k] = in[i * km + km + pos];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kMaxConv - 1; ++k)
+    if (k < km) out[i * km + k] = v[k];
 }
 
 }  // namespace
@@ -75,6 +111,20 @@ hipError_t launch_fwd_carry(const float* agg_h, const float* agg_s, const float*
   if (total <= 0) return hipSuccess;
   hipLaunchKernelGGL(carry_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s, agg_h, agg_s, A,
                      h_init, carry, batch, dim, N, nseg);
+  return hipGetLastError();
+}
+
+hipError_t launch_conv_state(const void* x, const float* in, float* out, int64_t batch, int64_t L, int64_t dim,
+                             int dconv, bool bf16, hipStream_t s) {
+  const int64_t n = batch * dim;
+  if (n <= 0 || dconv <= 1) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((n + 255) / 256));
+  if (bf16)
+    hipLaunchKernelGGL(conv_state_kernel<bf16_t>, grid, dim3(256), 0, s, static_cast<const bf16_t*>(x), in, out, batch, L,
+                       dim, dconv);
+  else
+    hipLaunchKernelGGL(conv_state_kernel<float>, grid, dim3(256), 0, s, static_cast<const float*>(x), in, out, batch, L,
+                       dim, dconv);
   return hipGetLastError();
 }
 

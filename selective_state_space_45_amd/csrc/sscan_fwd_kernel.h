@@ -118,13 +118,19 @@ __device__ __forceinline__ int64_t after(int64_t v, float dep) {
 // block of kBwdBlock steps is written to ckpt, for the backward pass).
 // NFIX: N as a compile-time constant (0 = read it from the shape at run time).
 // EULER: Bbar = Delta B instead of the zero-order hold.
-template <typename Tin, int NSPLIT, int NPW, int MODE, bool PAIR, int NFIX, bool EULER>
+// CONV: x is the raw input of a causal depthwise convolution over time (sh.dconv
+// taps, conv_w [dim][dconv], optional conv_b [dim]) followed by SiLU, as in the
+// page-3 report's MambaBlock (section 3, forward); the scan runs on its output.
+// Inputs before the sequence start come from conv_s [batch][dim][dconv-1] (zeros
+// when absent).
+template <typename Tin, int NSPLIT, int NPW, int MODE, bool PAIR, int NFIX, bool EULER, bool CONV>
 __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
     const Tin* __restrict__ xg, const Tin* __restrict__ dtg, const Tin* __restrict__ zg,
     const Tin* __restrict__ Bg, const Tin* __restrict__ Cg, const float* __restrict__ Ag,
     const float* __restrict__ Dg, const float* __restrict__ biasg, const float* __restrict__ h_init,
     Tin* __restrict__ yg, float* __restrict__ h_last, float* __restrict__ agg_h, float* __restrict__ agg_s,
-    float* __restrict__ ckpt, FwdShape sh) {
+    float* __restrict__ ckpt, const float* __restrict__ conv_w, const float* __restrict__ conv_b,
+    const float* __restrict__ conv_s, FwdShape sh) {
   constexpr bool AGG = MODE == kFwdAgg;
   constexpr bool OUT = MODE == kFwdOut;
   constexpr bool CKPT = MODE == kFwdCkpt;
@@ -215,6 +221,18 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
   }
 
   Tin rx[TPW], rdt[TPW], rz[TPW];
+  // CONV: raw inputs of the convolution window of each prologue timestep, and taps
+  constexpr int KC = CONV ? kMaxConv : 1;
+  Tin rxc[TPW][KC];
+  float cw[KC];
+  float cbias = 0.f;
+  const int K = CONV ? sh.dconv : 1;
+  const int lane_c = dvalid ? lane : 0;   // an in-range channel for lanes past dim
+  if constexpr (CONV) {
+#pragma unroll
+    for (int k = 0; k < KC; ++k) cw[k] = (k < K) ? conv_w[dd * K + k] : 0.f;
+    cbias = conv_b ? conv_b[dd] : 0.f;
+  }
   float eg[2][TPW], ed[2][TPW];
   float ssum = 0.f, scomp = 0.f;
   BRaw<Tin, PAIR, NPW> bc[T];
@@ -228,7 +246,7 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
       if (l < seg_n) {
         const int64_t off = static_cast<int64_t>(l) * dim;
         if (dvalid) {
-          a = (Xb + off)[lane];
+          if constexpr (!CONV) a = (Xb + off)[lane];
           e = (DTb + off)[lane];
           if (OUT && hasZ) f = (Zb + off)[lane];
         }
@@ -236,6 +254,20 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
       rx[i] = a;
       rdt[i] = e;
       rz[i] = f;
+      if constexpr (CONV) {
+        // window l - (K-1) .. l, loaded unconditionally from clamped in-range positions
+        // (no per-lane branches); positions before the sequence start are replaced
+        // from conv_s in the prologue, padded timesteps are discarded there
+        const int64_t lg = l_begin + l;
+        const int64_t lgc = lg < L ? lg : L - 1;
+        const Tin* __restrict__ Xrow = xg + b * L * dim + dtile * kTile;
+#pragma unroll
+        for (int k = 0; k < KC; ++k) {
+          const int back = (K - 1 - k) < 0 ? 0 : (K - 1 - k);
+          const int64_t pos = lgc - (back <= lgc ? back : lgc);
+          rxc[i][k] = (Xrow + pos * dim)[lane_c];
+        }
+      }
     }
   };
 
@@ -266,7 +298,24 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
     for (int i = 0; i < TPW; ++i) {
       const int t = w + NSPLIT * i;
       const bool lv = c * T + t < seg_n;
-      const float xv = to_f32(rx[i]);  // zero when out of range
+      float xv = to_f32(rx[i]);  // zero when out of range
+      if constexpr (CONV) {
+        const int64_t l_glob = l_begin + c * T + t;
+        float v[KC];
+#pragma unroll
+        for (int k = 0; k < KC; ++k) v[k] = to_f32(rxc[i][k]);
+        if (l_glob < K - 1) {   // wave-uniform: the window reaches before the sequence
+#pragma unroll
+          for (int k = 0; k < KC; ++k) {
+            const int64_t pos = l_glob - (K - 1) + k;
+            if (pos < 0) v[k] = (conv_s && dvalid) ? conv_s[(b * dim + d) * (K - 1) + (K - 1) + pos] : 0.f;
+          }
+        }
+        float acc = cbias;
+#pragma unroll
+        for (int k = 0; k < KC; ++k) acc = fmaf(cw[k], v[k], acc);   // taps past K are zero
+        xv = lv ? silu(acc) : 0.f;   // a padded step stays the identity
+      }
       float d2 = softplus_log2e(fmaf(to_f32(rdt[i]), kLog2e, bias2));
       d2 = lv ? d2 : 0.f;  // a padded step is the identity: Delta = 0, x = 0
       s_d2[P][t][lane] = d2;
@@ -468,34 +517,35 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
   }
 }
 
-template <typename Tin, int NS, int MODE, bool PR, int NF, bool EU>
+template <typename Tin, int NS, int MODE, bool PR, int NF, bool EU, bool CV>
 void launch_one(const FwdParams& p, dim3 grid, hipStream_t s) {
-  FwdShape sh{p.batch, p.L, p.dim, p.seg_len, p.ndtiles, p.nblk, p.N, p.nseg};
-  hipLaunchKernelGGL((fwd_kernel<Tin, NS, 1, MODE, PR, NF, EU>), grid, dim3(NS * 64), 0, s,
+  FwdShape sh{p.batch, p.L, p.dim, p.seg_len, p.ndtiles, p.nblk, p.N, p.nseg, p.dconv};
+  hipLaunchKernelGGL((fwd_kernel<Tin, NS, 1, MODE, PR, NF, EU, CV>), grid, dim3(NS * 64), 0, s,
                      static_cast<const Tin*>(p.x), static_cast<const Tin*>(p.dt), static_cast<const Tin*>(p.z),
                      static_cast<const Tin*>(p.B), static_cast<const Tin*>(p.C), p.A, p.Dskip, p.bias, p.h_init,
-                     static_cast<Tin*>(p.y), p.h_last, p.agg_h, p.agg_s, p.ckpt, sh);
+                     static_cast<Tin*>(p.y), p.h_last, p.agg_h, p.agg_s, p.ckpt, p.conv_w, p.conv_b, p.conv_s, sh);
 }
 
-template <typename Tin, int MODE, bool PR, bool EU>
+template <typename Tin, int MODE, bool PR, bool EU, bool CV>
 void launch_by_n(const FwdParams& p, dim3 grid, hipStream_t s) {
   switch (fwd_nsplit(p.N)) {
-    case 1: launch_one<Tin, 1, MODE, PR, 0, EU>(p, grid, s); break;
-    case 2: launch_one<Tin, 2, MODE, PR, 0, EU>(p, grid, s); break;
-    case 4: launch_one<Tin, 4, MODE, PR, 0, EU>(p, grid, s); break;
-    case 8: launch_one<Tin, 8, MODE, PR, 0, EU>(p, grid, s); break;
+    case 1: launch_one<Tin, 1, MODE, PR, 0, EU, CV>(p, grid, s); break;
+    case 2: launch_one<Tin, 2, MODE, PR, 0, EU, CV>(p, grid, s); break;
+    case 4: launch_one<Tin, 4, MODE, PR, 0, EU, CV>(p, grid, s); break;
+    case 8: launch_one<Tin, 8, MODE, PR, 0, EU, CV>(p, grid, s); break;
     default:
       if (p.N == 16)
-        launch_one<Tin, 16, MODE, PR, 16, EU>(p, grid, s);
+        launch_one<Tin, 16, MODE, PR, 16, EU, CV>(p, grid, s);
       else
-        launch_one<Tin, 16, MODE, PR, 0, EU>(p, grid, s);
+        launch_one<Tin, 16, MODE, PR, 0, EU, CV>(p, grid, s);
       break;
   }
 }
 
-// Launch of one (mode, discretization rule) variant; each variant is instantiated in
-// its own translation unit so the kernels compile in parallel.
-template <int MODE, bool EU>
+// Launch of one (mode, discretization rule, convolution prologue) variant; each
+// variant is instantiated in its own translation unit so the kernels compile in
+// parallel.
+template <int MODE, bool EU, bool CV>
 hipError_t launch_fwd_variant(const FwdParams& p, bool bf16, hipStream_t s) {
   const int64_t nblocks = p.ndtiles * p.batch * (MODE == kFwdAgg ? (p.nseg - 1) : p.nseg);
   if (nblocks <= 0) return hipSuccess;
@@ -503,11 +553,11 @@ hipError_t launch_fwd_variant(const FwdParams& p, bool bf16, hipStream_t s) {
   const bool pair = bf16 && (p.N % 2 == 0) && ((reinterpret_cast<uintptr_t>(p.B) & 3) == 0) &&
                     ((reinterpret_cast<uintptr_t>(p.C) & 3) == 0);
   if (!bf16)
-    launch_by_n<float, MODE, false, EU>(p, grid, s);
+    launch_by_n<float, MODE, false, EU, CV>(p, grid, s);
   else if (pair)
-    launch_by_n<bf16_t, MODE, true, EU>(p, grid, s);
+    launch_by_n<bf16_t, MODE, true, EU, CV>(p, grid, s);
   else
-    launch_by_n<bf16_t, MODE, false, EU>(p, grid, s);
+    launch_by_n<bf16_t, MODE, false, EU, CV>(p, grid, s);
   return hipGetLastError();
 }
 

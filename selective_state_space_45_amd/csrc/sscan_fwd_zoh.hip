@@ -3,8 +3,8 @@
 
 namespace sscan {
 
-template hipError_t launch_fwd_variant<kFwdOut, false>(const FwdParams&, bool, hipStream_t);
-template hipError_t launch_fwd_variant<kFwdAgg, false>(const FwdParams&, bool, hipStream_t);
-template hipError_t launch_fwd_variant<kFwdCkpt, false>(const FwdParams&, bool, hipStream_t);
+template hipError_t launch_fwd_variant<kFwdOut, false, false>(const FwdParams&, bool, hipStream_t);
+template hipError_t launch_fwd_variant<kFwdAgg, false, false>(const FwdParams&, bool, hipStream_t);
+template hipError_t launch_fwd_variant<kFwdCkpt, false, false>(const FwdParams&, bool, hipStream_t);
 
 }  // namespace sscan

@@ -9,6 +9,7 @@ namespace sscan {
 constexpr int kTile = 64;     // channels per workgroup: one per lane of a wave
 constexpr int kChunk = 16;    // timesteps staged through LDS per chunk
 constexpr int kBwdBlock = 8;  // timesteps per backward block = checkpoint spacing
+constexpr int kMaxConv = 4;   // taps of the fused convolution prologue (Mamba's d_conv)
 
 // Modes of the forward kernel.
 constexpr int kFwdOut = 0;    // y (and the final state)
@@ -31,6 +32,10 @@ struct FwdParams {
   float* agg_s;           // aggregate pass: [nseg][batch][dim]    sum of Delta*log2(e)
   float* ckpt;            // checkpoint pass: [batch][nblk][N][dim] state entering each block
   int64_t nblk;           // backward blocks over the whole sequence: ceil(L / kBwdBlock)
+  const float* conv_w;    // convolution prologue (nullable): taps [dim][dconv]
+  const float* conv_b;    // nullable: [dim]
+  const float* conv_s;    // nullable: raw inputs before the sequence [batch][dim][dconv-1]
+  int dconv;
   int64_t batch, L, dim;
   int64_t seg_len;        // timesteps per segment (multiple of kChunk unless nseg == 1)
   int64_t ndtiles;        // ceil(dim / kTile)
@@ -43,7 +48,7 @@ struct FwdParams {
 // restrict-qualified arguments so the compiler can keep B/C loads scalar).
 struct FwdShape {
   int64_t batch, L, dim, seg_len, ndtiles, nblk;
-  int N, nseg;
+  int N, nseg, dconv;
 };
 
 struct StepParams {
@@ -57,8 +62,12 @@ struct StepParams {
   const float* Dskip;
   const float* bias;
   void* y;
+  float* conv_state;      // convolution prologue (nullable): [batch][dim][dconv-1], in-out
+  const float* conv_w;    // [dim][dconv]
+  const float* conv_b;    // nullable: [dim]
   int64_t batch, dim;
   int N;
+  int dconv;
   bool euler;             // Bbar = Delta * B instead of the zero-order hold
 };
 
@@ -117,6 +126,10 @@ hipError_t launch_fwd_checkpoints(const FwdParams& p, bool bf16, hipStream_t s);
 hipError_t launch_fwd_carry(const float* agg_h, const float* agg_s, const float* A, const float* h_init,
                             float* carry, int64_t batch, int64_t dim, int N, int nseg, hipStream_t s);
 hipError_t launch_fill_state(float* dst, const float* src, int64_t n, hipStream_t s);
+// Convolution state after a sequence: the last dconv - 1 raw inputs (from x, or the
+// incoming state when seqlen < dconv - 1); out may equal in.
+hipError_t launch_conv_state(const void* x, const float* in, float* out, int64_t batch, int64_t L, int64_t dim,
+                             int dconv, bool bf16, hipStream_t s);
 hipError_t launch_step(const StepParams& p, bool bf16, hipStream_t s);
 
 }  // namespace sscan

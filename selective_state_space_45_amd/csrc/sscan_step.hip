@@ -5,6 +5,10 @@
 //   Delta = softplus(dt + bias), Abar = exp(Delta A), Bbar = (Abar - 1)/A * B
 //   (Delta * B when A == 0), h <- Abar h + Bbar x (in place), y = (C . h + D x) silu(z).
 // With the Euler rule (page-3 report, section 4.2) Bbar = Delta * B.
+// With the convolution prologue (page-3 report, section 6, MambaBlock.step), x is a
+// raw input: the scan runs on silu(conv_b + sum_k w[k] window[k]) over the window of
+// the dconv - 1 cached raw inputs and x, and the cache drops its oldest entry and
+// appends x.
 //
 // The step is bound by reading and writing the fp32 state [batch, dim, N].  Each
 // lane holds 8 (or 4) consecutive states of one (b, d) row, read and written with
@@ -36,13 +40,15 @@ __device__ __forceinline__ void load4(const Tin* __restrict__ p, int n0, int N, 
 // SPL states per lane (4 or 8), LPR = ceil(N / SPL) lanes per (b, d) row.  VEC: N is a
 // multiple of 4 and state, A, B, C allow 16-byte (8-byte for bf16 B/C) accesses.
 // NFIX: N as a compile-time constant (0 = run time).  EULER: Bbar = Delta B.
-template <typename Tin, int SPL, int LPR, bool VEC, int NFIX, bool EULER>
+// CONV: convolution prologue with cache cst [rows][dconv-1], taps cw [dim][dconv].
+template <typename Tin, int SPL, int LPR, bool VEC, int NFIX, bool EULER, bool CONV>
 __global__ __launch_bounds__(256) void step_kernel(float* __restrict__ S, const Tin* __restrict__ X,
                                                    const Tin* __restrict__ DT, const Tin* __restrict__ Z,
                                                    const Tin* __restrict__ Bp, const Tin* __restrict__ Cp,
                                                    const float* __restrict__ Ag, const float* __restrict__ Dg,
                                                    const float* __restrict__ biasg, Tin* __restrict__ Y, int64_t rows,
-                                                   int64_t dim, int Nrt) {
+                                                   int64_t dim, int Nrt, float* __restrict__ cst,
+                                                   const float* __restrict__ cw, const float* __restrict__ cb, int K) {
   const int N = NFIX > 0 ? NFIX : Nrt;
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int64_t row = gid / LPR;
@@ -52,7 +58,26 @@ __global__ __launch_bounds__(256) void step_kernel(float* __restrict__ S, const 
   const int n0 = SPL * q;
 
   float yp = 0.f;
-  const float xv = to_f32(X[row]);
+  float xv = to_f32(X[row]);
+  if constexpr (CONV) {
+    // window: cached raw inputs (oldest first) then x; read before any lane updates it
+    float* cs = cst + row * (K - 1);
+    float win[kMaxConv];
+#pragma unroll
+    for (int k = 0; k < kMaxConv; ++k) win[k] = (k < K - 1) ? cs[k] : 0.f;
+    float acc = cb ? cb[d] : 0.f;
+#pragma unroll
+    for (int k = 0; k < kMaxConv; ++k) {
+      const float v = (k < K - 1) ? win[k] : xv;
+      if (k < K) acc = fmaf(cw[d * K + k], v, acc);
+    }
+    if (q == 0) {
+#pragma unroll
+      for (int k = 0; k < kMaxConv - 1; ++k)
+        if (k < K - 1) cs[k] = (k + 1 < K - 1) ? win[k + 1] : xv;
+    }
+    xv = silu(acc);
+  }
   if (n0 < N) {
     const float v2 = fmaf(to_f32(DT[row]), kLog2e, biasg ? biasg[d] * kLog2e : 0.f);
     float h[SPL], a[SPL], bv[SPL], cv[SPL];
@@ -111,10 +136,18 @@ template <typename Tin, int SPL, int LPR, bool VEC, int NF, bool EU>
 void launch_step_one(const StepParams& p, hipStream_t s) {
   const int64_t rows = p.batch * p.dim;
   const int64_t threads = rows * LPR;
-  hipLaunchKernelGGL((step_kernel<Tin, SPL, LPR, VEC, NF, EU>), dim3(static_cast<unsigned>((threads + 255) / 256)),
+  if (p.conv_w) {
+    hipLaunchKernelGGL((step_kernel<Tin, SPL, LPR, VEC, NF, EU, true>), dim3(static_cast<unsigned>((threads + 255) / 256)),
+                       dim3(256), 0, s, p.state, static_cast<const Tin*>(p.x), static_cast<const Tin*>(p.dt),
+                       static_cast<const Tin*>(p.z), static_cast<const Tin*>(p.B), static_cast<const Tin*>(p.C), p.A,
+                       p.Dskip, p.bias, static_cast<Tin*>(p.y), rows, p.dim, p.N, p.conv_state, p.conv_w, p.conv_b,
+                       p.dconv);
+    return;
+  }
+  hipLaunchKernelGGL((step_kernel<Tin, SPL, LPR, VEC, NF, EU, false>), dim3(static_cast<unsigned>((threads + 255) / 256)),
                      dim3(256), 0, s, p.state, static_cast<const Tin*>(p.x), static_cast<const Tin*>(p.dt),
                      static_cast<const Tin*>(p.z), static_cast<const Tin*>(p.B), static_cast<const Tin*>(p.C), p.A,
-                     p.Dskip, p.bias, static_cast<Tin*>(p.y), rows, p.dim, p.N);
+                     p.Dskip, p.bias, static_cast<Tin*>(p.y), rows, p.dim, p.N, nullptr, nullptr, nullptr, 1);
 }
 
 template <typename Tin, bool EU>

@@ -27,6 +27,8 @@ def lib():
     lb.sscan_bwd_workspace_size.argtypes = [I64, I64, I64, I64, ctypes.c_int]
     lb.sscan_bwd_workspace_size.restype = SZ
     lb.sscan_bwd.argtypes = [I64, I64, I64, I64, ctypes.c_int, U32] + [P] * 21 + [SZ, P]
+    lb.sscan_fwd_conv.argtypes = [I64, I64, I64, I64, I64, ctypes.c_int, U32] + [P] * 15 + [P, SZ, P]
+    lb.sscan_step_conv.argtypes = [I64, I64, I64, I64, ctypes.c_int, U32] + [P] * 14
     return lb
 
 
@@ -39,7 +41,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for must in ("sscan_fwd", "sscan_step", "sscan_fwd_segmented", "sscan_fwd_workspace_size",
-                 "sscan_bwd", "sscan_bwd_workspace_size", "sscan_last_error", "sscan_version"):
+                 "sscan_bwd", "sscan_bwd_workspace_size", "sscan_fwd_conv", "sscan_step_conv",
+                 "sscan_last_error", "sscan_version"):
         assert must in names
 
 
@@ -172,3 +175,24 @@ def test_bwd_workspace_size_grows_with_the_problem(lib):
     parts = 2 * 32 * 8 * 16 * 4096 * 4
     assert a >= ckpt + parts
     assert lib.sscan_bwd_workspace_size(8, 0, 2048, 16, 1) == 0
+
+
+def test_conv_validation(lib):
+    P = ctypes.c_void_p
+
+    def fc(dconv=4, w=P(0x90000), **kw):
+        a = dict(batch=2, L=8, dim=4, N=4)
+        a.update(kw)
+        return lib.sscan_fwd_conv(a["batch"], a["L"], a["dim"], a["N"], dconv, 0, 0, FAKE, w, None, None, None, FAKE2,
+                                  P(0x30000), P(0x40000), P(0x50000), None, None, None, None, P(0x60000), None, None, 0,
+                                  None)
+    assert fc(dconv=5) == 2 and b"dconv" in lib.sscan_last_error()
+    assert fc(dconv=0) == 2
+    assert fc(w=None) == 1
+    assert fc(batch=0) == 0
+    # step: conv_state required when dconv > 1
+    args = [P(0x10000), None, P(0x20000), P(0x90000), None, P(0x30000), P(0x40000), P(0x50000), P(0x60000), None,
+            None, None, P(0x70000), None]
+    assert lib.sscan_step_conv(4, 8, 4, 4, 0, 0, *args) == 1
+    assert b"conv_state" in lib.sscan_last_error()
+    assert lib.sscan_step_conv(4, 8, 4, 9, 0, 0, *args) == 2
