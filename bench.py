@@ -9,6 +9,7 @@ timed region.  One JSON line is printed.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
                     [--no-euler] [--no-bwd] [--no-conv] [--copy-calibration]
     python bench.py --summarize-counters FETCH_CSV WRITE_CSV   (CPU only)
+    python bench.py --configs     (one line per workload: GPU time, GB/s, oracle time, error)
 
 --copy-calibration also runs a plain 512 MiB -> 512 MiB elementwise copy (three
 times), the known-size reference that scales the HBM byte counters read by
@@ -105,7 +106,97 @@ def summarize_counters(fetch_csv: str, write_csv: str) -> dict:
             "traffic_over_algorithmic": round((rd + wr) / alg, 4)}
 
 
+def per_config_report() -> None:
+    """One JSON line per workload (documentation mode, --configs): GPU time (median of
+    HIP-event-timed launches, inputs resident), effective GB/s, the oracle's time on the
+    host cores, and the max error against the oracle under the parity-test metric."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import selective_state_space_45_amd as ss
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def tens(a, dtype):
+        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+        return t.to(torch.bfloat16) if dtype == "bf16" else t
+
+    def median_ms(fn, n=20, warm=3):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(n):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    for name in ("tiny", "mamba130m_layer", "train_shape", "long_context"):
+        w = W.workload(name)
+        x, dt, z, B, C = (tens(a, w.dtype) for a in (w.x, w.dt, w.z, w.B, w.C))
+        A, D, bias = tens(w.A, "f32"), tens(w.D, "f32"), (None if w.dt_bias is None else tens(w.dt_bias, "f32"))
+        y = torch.empty_like(x)
+        st = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev)
+        wsb = ss.fwd_workspace_size(w.batch, w.seqlen, w.dim, w.dstate, x.dtype)
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+        run = lambda: ss.sscan_fwd(x, dt, A, B, C, D=D, z=z, delta_bias=bias, out=y, last_state=st, workspace=ws)
+        ms = median_ms(run)
+        nb = W.fwd_algorithmic_bytes(w.batch, w.seqlen, w.dim, w.dstate, w.dtype)
+        t0 = time.perf_counter()
+        yr, sr = oracle.sscan_fwd(w.x, w.dt, w.A, w.B, w.C, D=w.D, z=w.z, dt_bias=w.dt_bias)
+        cpu_s = time.perf_counter() - t0
+        run()
+        torch.cuda.synchronize()
+        yg = y.float().cpu().numpy()
+        err = float(np.max(np.abs(yg - yr) / (1.0 + np.abs(yr))))
+        es = float(np.max(np.abs(st.cpu().numpy() - sr) / (1.0 + np.abs(sr))))
+        tokch = w.batch * w.seqlen * w.dim
+        print(json.dumps({"config": name, "shape": [w.batch, w.seqlen, w.dim, w.dstate], "dtype": w.dtype,
+                          "gpu_ms_median": round(ms, 5), "tokens_channels_per_s": round(tokch / (ms * 1e-3), 1),
+                          "gbs": round(nb / (ms * 1e-3) / 1e9, 2), "hbm_frac": round(nb / (ms * 1e-3) / 1e9 / 8000, 4),
+                          "segments": "auto" if wsb else 1, "max_err_y": err, "max_err_state": es,
+                          "tol": 1e-4 if w.dtype == "f32" else 2e-2, "oracle_s": round(cpu_s, 3),
+                          "oracle_threads": oracle.last_threads_used(),
+                          "oracle_tokens_channels_per_s": round(tokch / cpu_s, 1)}), flush=True)
+        del x, dt, z, B, C, y, st, ws
+
+    dw = W.DecodeWorkload()
+    tk = dw.token(0)
+    sd = tens(dw.state0, "f32")
+    tx, tdt, tz, tB, tC = (tens(a, "bf16") for a in (tk.x, tk.dt, tk.z, tk.B, tk.C))
+    dA, dD = tens(dw.A, "f32"), tens(dw.D, "f32")
+    yd = torch.empty_like(tx)
+    g = torch.cuda.CUDAGraph()
+    for _ in range(3):
+        ss.sscan_step(sd, tx, tdt, dA, tB, tC, D=dD, z=tz, out=yd)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for _ in range(20):
+            ss.sscan_step(sd, tx, tdt, dA, tB, tC, D=dD, z=tz, out=yd)
+    ms = median_ms(g.replay) / 20
+    st_ref = dw.state0.astype(np.float64)
+    t0 = time.perf_counter()
+    oracle.sscan_step(st_ref, tk.x, tk.dt, dw.A, tk.B, tk.C, D=dw.D, z=tk.z)
+    cpu_s = time.perf_counter() - t0
+    nb = W.step_algorithmic_bytes(dw.batch, dw.dim, dw.dstate, "bf16")
+    print(json.dumps({"config": "decode_step", "shape": [dw.batch, dw.dim, dw.dstate], "dtype": "bf16",
+                      "gpu_us_per_step_median": round(ms * 1e3, 2), "gbs": round(nb / (ms * 1e-3) / 1e9, 2),
+                      "hbm_frac": round(nb / (ms * 1e-3) / 1e9 / 8000, 4), "oracle_s_per_step": round(cpu_s, 4),
+                      "oracle_threads": oracle.last_threads_used(),
+                      "note": "errors over 1000 steps are checked by the parity tests"}), flush=True)
+
+
 def main():
+    if len(sys.argv) == 2 and sys.argv[1] == "--configs":
+        per_config_report()
+        return
     if len(sys.argv) == 4 and sys.argv[1] == "--summarize-counters":
         out = summarize_counters(sys.argv[2], sys.argv[3])
         with open(PROFILE_SUMMARY, "w") as f:
