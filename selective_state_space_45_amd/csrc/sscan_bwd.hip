@@ -34,6 +34,9 @@
 //   P5  each wave sums the terms over states for its timesteps and stores dx, ddt.
 // dB and dC leave as per-tile partial sums, dA, dD and dbias as per-batch-row
 // partial sums; small reduction kernels finish them in a fixed order.
+#include <type_traits>
+
+#include "selscan.h"
 #include "sscan_device.h"
 #include "sscan_internal.h"
 
@@ -57,6 +60,13 @@ constexpr int kDppRowRor8 = 0x128;        // lane i <- row lane (i + 8) mod 16: 
 constexpr int kDppRowHalfMirror = 0x141;  // lane i <- 7 - i within each 8 lanes: partner i ^ 7
 constexpr int kDppQuadXor2 = 0x4e;        // quad_perm [2,3,0,1]
 constexpr int kDppQuadXor1 = 0xb1;        // quad_perm [1,0,3,2]
+
+__device__ __forceinline__ void unpack(const float4& v, float* o) {
+  o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+}
+__device__ __forceinline__ void unpack(const float2& v, float* o) {
+  o[0] = v.x; o[1] = v.y;
+}
 
 // One halving step of a butterfly reduce-scatter through a DPP permutation that
 // pairs every lane with a partner whose BIT differs: lanes with BIT clear keep
@@ -93,6 +103,34 @@ __device__ __forceinline__ void lane_reduce32(float* v, int lane) {
   v[0] += dpp<kDppQuadXor1>(v[0]);
 }
 
+// Sum of v[0..15] over the 64 lanes of a wave, as a reduce-scatter: afterwards lane
+// L holds in v[0] the total of element L >> 2 (all four lanes of a quad agree).
+__device__ __forceinline__ void lane_reduce16(float* v, int lane) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[k]), __float_as_uint(v[k + 8]), false, false);
+    v[k] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[k]), __float_as_uint(v[k + 4]), false, false);
+    v[k] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  halve_dpp<kDppRowRor8, 8, 2>(v, lane);
+  halve_dpp<kDppRowHalfMirror, 4, 1>(v, lane);
+  v[0] += dpp<kDppQuadXor2>(v[0]);
+  v[0] += dpp<kDppQuadXor1>(v[0]);
+}
+
+// Reduce-scatter of S * kBwdBlock values: element k ends in lanes (k << SH) .. ((k+1) << SH) - 1.
+template <int NV>
+__device__ __forceinline__ void lane_reduce(float* v, int lane) {
+  if constexpr (NV == 32)
+    lane_reduce32(v, lane);
+  else
+    lane_reduce16(v, lane);
+}
+
 // (u e^u - e^u + 1) / u^2 by its Taylor series sum_k (k+1) u^k / (k+2)!, |u| < 0.5.
 __device__ __forceinline__ float dphi1_series(float u) {
   float r = 1.f / 5760.f;
@@ -106,9 +144,13 @@ __device__ __forceinline__ float dphi1_series(float u) {
 
 }  // namespace
 
-// Waves per workgroup of the backward kernel: four states per wave.
-constexpr int kBwdSpw = 4;
-inline int bwd_waves(int N) { return N <= 4 ? 1 : (N <= 8 ? 2 : 4); }
+// States per wave of the backward kernel, and waves per workgroup for a given N.
+constexpr int kBwdSpw = 2;
+inline int bwd_waves(int N) {
+  int w = 1;
+  while (w * kBwdSpw < N) w <<= 1;
+  return w;
+}
 
 template <typename Tin, int NW, int NFIX, bool EULER>
 __global__ __launch_bounds__(NW * 64) void bwd_kernel(
@@ -123,15 +165,19 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(
   constexpr int S = kBwdSpw;          // states per wave
   constexpr int NSP = NW * S;         // states covered (N rounded up)
   constexpr int TPW = T / NW;         // prologue / epilogue timesteps per wave
-  static_assert(T * S == 32, "a block's terms of one wave fill one 32-value lane reduction");
+  static_assert(T * S == 32 || T * S == 16, "a block's terms of one wave fill one lane reduction");
+  constexpr int NV = T * S;                 // values per lane reduction
+  constexpr int SH = NV == 32 ? 1 : 2;      // lanes per reduced element: 1 << SH
   static_assert(T % NW == 0, "block must split evenly over waves");
 
   // staging of one block, double-buffered (P1 of block j-1 overlaps P5 of block j)
   __shared__ float s_d2[2][T][kTile];     // Delta * log2(e)
   __shared__ float s_xv[2][T][kTile];     // x
   __shared__ float s_go[2][T][kTile];     // gyo = dy * silu(z)
-  __shared__ float4 s_B[2][T][NSP / 4];   // B and C of the block, four states per float4
-  __shared__ float4 s_C[2][T][NSP / 4];
+  // B and C of the block, S consecutive states per vector
+  using VS = typename std::conditional<S == 4, float4, float2>::type;
+  __shared__ VS s_B[2][T][NSP / S];
+  __shared__ VS s_C[2][T][NSP / S];
   // per-wave partial sums over its states: C.h (readout), dx terms, dDelta terms
   __shared__ float s_r0[NW][T][kTile];
   __shared__ float s_r1[NW][T][kTile];
@@ -265,10 +311,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(
           const float d2 = s_d2[pb][t][lane];
           const float xv = s_xv[pb][t][lane];
           const float go = s_go[pb][t][lane];
-          const float4 b4 = s_B[pb][t][w];
-          const float4 c4 = s_C[pb][t][w];
-          const float bq[S] = {b4.x, b4.y, b4.z, b4.w};
-          const float cq[S] = {c4.x, c4.y, c4.z, c4.w};
+          float bq[S], cq[S];
+          unpack(s_B[pb][t][w], bq);
+          unpack(s_C[pb][t][w], cq);
           float yo = 0.f;
 #pragma unroll
           for (int q = 0; q < S; ++q) {
@@ -294,9 +339,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(
         recompute(std::false_type{});
       else
         recompute(std::true_type{});
-      lane_reduce32(red, lane);
-      if ((lane & 1) == 0) {
-        const int k = lane >> 1, q = k / T, t = k % T;
+      lane_reduce<NV>(red, lane);
+      if ((lane & ((1 << SH) - 1)) == 0) {
+        const int k = lane >> SH, q = k / T, t = k % T;
         if (n0 + q < N && t < cnt) gCp[part + (n0 + q) * L + t] = red[0];
       }
     }
@@ -311,10 +356,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(
         const float go = s_go[pb][t][lane];
         const float d2 = s_d2[pb][t][lane];
         const float xv = s_xv[pb][t][lane];
-        const float4 b4 = s_B[pb][t][w];
-        const float4 c4 = s_C[pb][t][w];
-        const float bq[S] = {b4.x, b4.y, b4.z, b4.w};
-        const float cq[S] = {c4.x, c4.y, c4.z, c4.w};
+        float bq[S], cq[S];
+        unpack(s_B[pb][t][w], bq);
+        unpack(s_C[pb][t][w], cq);
         const float delta = d2 * kLn2;
         float r1 = 0.f, r2 = 0.f;
 #pragma unroll
@@ -363,9 +407,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(
         for (int q = 0; q < S; ++q) asm volatile("" : "+v"(gA[q]));
         __builtin_amdgcn_sched_barrier(0);
       }
-      lane_reduce32(red, lane);
-      if ((lane & 1) == 0) {
-        const int k = lane >> 1, q = k / T, t = k % T;
+      lane_reduce<NV>(red, lane);
+      if ((lane & ((1 << SH) - 1)) == 0) {
+        const int k = lane >> SH, q = k / T, t = k % T;
         if (n0 + q < N && t < cnt) gBp[part + (n0 + q) * L + t] = red[0];
       }
     }
@@ -610,14 +654,16 @@ void launch_bwd_one(const BwdParams& p, hipStream_t s) {
 
 template <typename Tin, bool EU>
 void launch_bwd_n(const BwdParams& p, hipStream_t s) {
+  constexpr int WMAX = SSCAN_MAX_DSTATE / kBwdSpw;
   switch (bwd_waves(p.N)) {
     case 1: launch_bwd_one<Tin, 1, 0, EU>(p, s); break;
     case 2: launch_bwd_one<Tin, 2, 0, EU>(p, s); break;
+    case 4: launch_bwd_one<Tin, 4, 0, EU>(p, s); break;
     default:
       if (p.N == 16)
-        launch_bwd_one<Tin, 4, 16, EU>(p, s);
+        launch_bwd_one<Tin, WMAX, 16, EU>(p, s);
       else
-        launch_bwd_one<Tin, 4, 0, EU>(p, s);
+        launch_bwd_one<Tin, WMAX, 0, EU>(p, s);
       break;
   }
 }
