@@ -230,29 +230,58 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(
   float e_sig[TPW], e_gz[TPW];                       // epilogue values of this wave's timesteps
   float accD = 0.f, accBias = 0.f;
 
-  // P1: x, dt, z, dy of this wave's timesteps of block j; Delta, x, gyo to LDS
-  // buffer j & 1 with the block's B and C rows.
+  // Global inputs of one block, loaded one block ahead of their use: x, dt, z, dy of
+  // this wave's timesteps, one B and one C element of the block's rows, and this
+  // wave's checkpoint states.
+  Tin r_x[TPW], r_dt[TPW], r_z[TPW], r_dy[TPW];
+  Tin r_b = Tin(0), r_c = Tin(0);
+  float r_ck[S];
+  const int bc_t = tid / NSP, bc_n = tid - (tid / NSP) * NSP;   // B/C element this thread stages
+  const bool bc_stager = tid < T * NSP;
+  auto gload = [&](int64_t j) {
+    const int64_t l0 = j * T;
+    const int cnt = static_cast<int>((L - l0) < T ? (L - l0) : T);
+    const int64_t base = tok_b + l0 * dim;
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int t = w + NW * i;
+      Tin a = Tin(0), e = Tin(0), f = Tin(0), g = Tin(0);
+      if (dvalid && t < cnt) {
+        const int off = t * dim32 + lane;
+        a = (xg + base)[off];
+        e = (dtg + base)[off];
+        g = (dyg + base)[off];
+        if (hasZ) f = (zg + base)[off];
+      }
+      r_x[i] = a;
+      r_dt[i] = e;
+      r_z[i] = f;
+      r_dy[i] = g;
+    }
+    r_b = Tin(0);
+    r_c = Tin(0);
+    if (bc_stager && bc_n < N && bc_t < cnt) {
+      const int64_t r = (b * L + l0 + bc_t) * N + bc_n;
+      r_b = Bg[r];
+      r_c = Cg[r];
+    }
+    const float* ck = ckpt + ((b * sh.nblk + j) * N) * dim + dtile * kTile;
+#pragma unroll
+    for (int q = 0; q < S; ++q) r_ck[q] = (n0 + q < N && dvalid) ? ck[(n0 + q) * dim + lane] : 0.f;
+  };
+
+  // P1: from the prefetched inputs of block j: Delta, x, gyo to LDS buffer j & 1 with
+  // the block's B and C rows; silu'(z) and sigmoid(dt + bias) kept for P5.
+  float h_next[S];
   auto prologue = [&](int64_t j) {
     const int pb = static_cast<int>(j & 1);
     const int64_t l0 = j * T;
     const int cnt = static_cast<int>((L - l0) < T ? (L - l0) : T);
-    const int64_t base = tok_b + l0 * dim;
-    const Tin* __restrict__ xb = xg + base;
-    const Tin* __restrict__ dtb = dtg + base;
-    const Tin* __restrict__ dyb = dyg + base;
-    const Tin* __restrict__ zb = hasZ ? zg + base : nullptr;
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int t = w + NW * i;
-      float xv = 0.f, dtv = 0.f, zv = 0.f, gy = 0.f;
-      if (dvalid && t < cnt) {
-        const int off = t * dim32 + lane;
-        xv = to_f32(xb[off]);
-        dtv = to_f32(dtb[off]);
-        gy = to_f32(dyb[off]);
-        if (hasZ) zv = to_f32(zb[off]);
-      }
-      const float v2 = fmaf(dtv, kLog2e, bias2);
+      const float xv = to_f32(r_x[i]), zv = to_f32(r_z[i]), gy = to_f32(r_dy[i]);
+      const float v2 = fmaf(to_f32(r_dt[i]), kLog2e, bias2);
       float gyo = gy, gz = 0.f;
       if (hasZ) {
         const float sg = hw_rcp(1.f + hw_exp2(-zv * kLog2e));
@@ -265,26 +294,22 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(
       e_gz[i] = gz;
       e_sig[i] = hw_rcp(1.f + hw_exp2(-v2));  // sigmoid(dt + bias) = softplus'
     }
-    const Tin* __restrict__ Bb = Bg + (b * L + l0) * N;
-    const Tin* __restrict__ Cb = Cg + (b * L + l0) * N;
-    float* sB = reinterpret_cast<float*>(s_B[pb]);
-    float* sC = reinterpret_cast<float*>(s_C[pb]);
-    for (int i = tid; i < T * NSP; i += NW * 64) {
-      const int t = i / NSP, nn = i - t * NSP;
-      float bv = 0.f, cv = 0.f;
-      if (nn < N && t < cnt) {
-        bv = to_f32(Bb[t * N + nn]);
-        cv = to_f32(Cb[t * N + nn]);
-      }
-      sB[i] = bv;
-      sC[i] = cv;
+    if (bc_stager) {
+      reinterpret_cast<float*>(s_B[pb])[tid] = to_f32(r_b);
+      reinterpret_cast<float*>(s_C[pb])[tid] = to_f32(r_c);
     }
+#pragma unroll
+    for (int q = 0; q < S; ++q) h_next[q] = r_ck[q];
   };
 
   const int64_t nblk = sh.nblk;
   const int64_t jbeg = static_cast<int64_t>(seg) * sh.seg_blocks;
   const int64_t jend = (jbeg + sh.seg_blocks < nblk) ? jbeg + sh.seg_blocks : nblk;
-  if (jend > jbeg) prologue(jend - 1);
+  if (jend > jbeg) {
+    gload(jend - 1);
+    prologue(jend - 1);
+    if (jend - 2 >= jbeg) gload(jend - 2);
+  }
   for (int64_t j = jend - 1; j >= jbeg; --j) {
     const int pb = static_cast<int>(j & 1);
     const int64_t l0 = j * T;
@@ -292,11 +317,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(
     const int64_t tok_blk = tok_b + l0 * dim;
     const int64_t part = (dtile * sh.batch + b) * N * L + l0;   // + n * L + t: partials of dB, dC
     float h[S];
-    {
-      const float* ck = ckpt + ((b * nblk + j) * N) * dim + dtile * kTile;
 #pragma unroll
-      for (int q = 0; q < S; ++q) h[q] = (n0 + q < N && dvalid) ? ck[(n0 + q) * dim + lane] : 0.f;
-    }
+    for (int q = 0; q < S; ++q) h[q] = h_next[q];
     __syncthreads();
 
     // ---- P2: recompute the block's states from the checkpoint; partial C.h of the
@@ -444,7 +466,10 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(
         accBias += gdt;
       }
     }
-    if (j > jbeg) prologue(j - 1);
+    if (j > jbeg) {
+      prologue(j - 1);
+      if (j - 2 >= jbeg) gload(j - 2);
+    }
   }
 
   // per-(segment, batch row) partial sums of dA, dD and dbias
@@ -517,30 +542,49 @@ __global__ __launch_bounds__(NW * 64) void bwd_agg_kernel(
   const int64_t l_end = (l_beg + sh.seg_blocks * kBwdBlock < L) ? l_beg + sh.seg_blocks * kBwdBlock : L;
   const int64_t nb = (l_end - l_beg + T - 1) / T;
   const int64_t tok_b = b * L * dim + dtile * kTile;
-  for (int64_t c = nb - 1; c >= 0; --c) {
+  // inputs of one block, loaded one block ahead of their use
+  Tin r_dt[TPW], r_z[TPW], r_dy[TPW];
+  Tin r_c = Tin(0);
+  const int c_n = tid / T, c_t = tid - (tid / T) * T;   // C element this thread stages
+  const bool c_stager = tid < T * NW;                    // [NW][T] elements, half the threads
+  auto gload = [&](int64_t c) {
     const int64_t l0 = l_beg + c * T;
     const int cnt = static_cast<int>((l_end - l0) < T ? (l_end - l0) : T);
     const int64_t base = tok_b + l0 * dim;
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int t = w + NW * i;
-      float dtv = 0.f, zv = 0.f, gy = 0.f;
+      Tin e = Tin(0), f = Tin(0), g = Tin(0);
       if (dvalid && t < cnt) {
         const int off = t * dim32 + lane;
-        dtv = to_f32((dtg + base)[off]);
-        gy = to_f32((dyg + base)[off]);
-        if (hasZ) zv = to_f32((zg + base)[off]);
+        e = (dtg + base)[off];
+        g = (dyg + base)[off];
+        if (hasZ) f = (zg + base)[off];
       }
+      r_dt[i] = e;
+      r_z[i] = f;
+      r_dy[i] = g;
+    }
+    r_c = (c_stager && c_n < N && c_t < cnt) ? Cg[(b * L + l0 + c_t) * N + c_n] : Tin(0);
+  };
+  auto prologue = [&](int64_t c) {
+    const int64_t l0 = l_beg + c * T;
+    const int cnt = static_cast<int>((l_end - l0) < T ? (l_end - l0) : T);
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int t = w + NW * i;
+      const float zv = to_f32(r_z[i]), gy = to_f32(r_dy[i]);
       float go = gy;
       if (hasZ) go = gy * (zv * hw_rcp(1.f + hw_exp2(-zv * kLog2e)));
-      s_d2[t][lane] = (t < cnt) ? softplus_log2e(fmaf(dtv, kLog2e, bias2)) : 0.f;
+      s_d2[t][lane] = (t < cnt) ? softplus_log2e(fmaf(to_f32(r_dt[i]), kLog2e, bias2)) : 0.f;
       s_go[t][lane] = go;
     }
-    const Tin* __restrict__ Cb = Cg + (b * L + l0) * N;
-    for (int i = tid; i < T * NW; i += NW * 64) {
-      const int nn = i / T, t = i - nn * T;
-      s_C[nn][t] = (nn < N && t < cnt) ? to_f32(Cb[t * N + nn]) : 0.f;
-    }
+    if (c_stager) s_C[c_n][c_t] = to_f32(r_c);
+  };
+  if (nb > 0) gload(nb - 1);
+  for (int64_t c = nb - 1; c >= 0; --c) {
+    prologue(c);
+    if (c > 0) gload(c - 1);
     __syncthreads();
 #pragma unroll 8
     for (int t = T - 1; t >= 0; --t) {
