@@ -61,19 +61,37 @@ size_t seg_workspace_bytes(int64_t batch, int64_t dim, int64_t N, int nseg) {
   return static_cast<size_t>(nseg) * batch * dim * (2 * N + 1) * sizeof(float);
 }
 
-// Segments wanted for a shape: one unless the (batch, channel-tile) grid alone
-// leaves compute units idle; then enough for about two workgroups per CU, with
-// segments of at least four chunks.
+// Segment count for a (batch, channel-tile) grid of `base` workgroups over `seqlen`
+// steps, when `per_round` workgroups run at once (resident per CU x CUs).  One
+// segment if the grid alone fills a round.  Otherwise the count, between the one
+// that gives two rounds of workgroups and four times that (and with segments of at
+// least min_len steps), whose last round is fullest: a grid just past a multiple of
+// the round leaves a nearly empty last round, measured at up to 30 % slower.
+int64_t pick_segments(int64_t base, int64_t seqlen, int64_t per_round, int64_t min_len) {
+  if (base <= 0 || base >= per_round) return 1;
+  const int64_t lo = (2 * per_round + base - 1) / base;
+  int64_t hi = 4 * lo;
+  const int64_t cap = seqlen / min_len < 1024 ? seqlen / min_len : 1024;
+  if (hi > cap) hi = cap;
+  if (lo > hi) return hi < 1 ? 1 : hi;
+  int64_t best = lo;
+  double best_fill = -1.0;
+  for (int64_t n = lo; n <= hi; ++n) {
+    const int64_t wgs = base * n;
+    const int64_t rounds = (wgs + per_round - 1) / per_round;
+    const double fill = static_cast<double>(wgs) / static_cast<double>(rounds * per_round);
+    if (fill > best_fill + 1e-9) {
+      best_fill = fill;
+      best = n;
+    }
+  }
+  return best;
+}
+
+// Forward: the main pass runs one 16-wave workgroup per CU (its LDS use).
 int auto_segments(int64_t batch, int64_t seqlen, int64_t dim) {
   const int64_t ndt = (dim + sscan::kTile - 1) / sscan::kTile;
-  const int64_t base = ndt * batch;
-  const int64_t cus = device_cus();
-  if (base <= 0 || base >= cus) return 1;
-  int64_t want = (2 * cus + base - 1) / base;
-  const int64_t maxseg = seqlen / (4 * sscan::kChunk);
-  if (want > maxseg) want = maxseg;
-  if (want > 1024) want = 1024;
-  return want < 1 ? 1 : static_cast<int>(want);
+  return static_cast<int>(pick_segments(ndt * batch, seqlen, device_cus(), 4 * sscan::kChunk));
 }
 
 SegPlan plan_segments(int64_t batch, int64_t seqlen, int64_t dim, int64_t N, int64_t requested,
@@ -267,19 +285,14 @@ struct BwdLayout {
   int64_t seg_blocks;      // kBwdBlock-step blocks per reverse segment
 };
 
-// Reverse-pass segments: the reverse kernel has four waves per workgroup and two
-// workgroups fit a CU, so split the sequence until the (batch, channel tile, segment)
-// grid gives about two workgroups per CU, with segments of at least 64 steps.
+// Reverse-pass segments: two reverse-kernel workgroups are resident per CU (LDS).
 int bwd_segments(int64_t batch, int64_t seqlen, int64_t dim) {
   const int64_t ndt = (dim + sscan::kTile - 1) / sscan::kTile;
   const int64_t base = ndt * batch;
   const int64_t cus = device_cus();
   if (base <= 0) return 1;
-  int64_t want = (2 * cus + base - 1) / base;
-  const int64_t maxseg = seqlen / 64;
-  if (want > maxseg) want = maxseg;
-  if (want > 1024) want = 1024;
-  return want < 1 ? 1 : static_cast<int>(want);
+  if (base >= cus) return base >= 2 * cus ? 1 : 2;   // two segments fill the second slot per CU
+  return static_cast<int>(pick_segments(base, seqlen, 2 * cus, 64));
 }
 
 BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t N) {
