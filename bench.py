@@ -35,6 +35,7 @@ PEAK_VALU_TOPS = 256 * 64 * 2.4e9 / 1e12
 OPS_PER_STATE_UPDATE = 8     # Delta*A, exp (2), B/A scale, x scale, add, fma (state), fma (readout)
 OPS_PER_TOKEN_CHANNEL = 20   # softplus 11, silu 7, skip + gate 2
 PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "sscan_fwd_train_shape_counters.json")
+COPY_ELEMS = 128 << 20                       # calibration copy: 512 MiB of fp32
 KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_45_amd", "csrc", f)
                   for f in ("sscan_fwd_kernel.h", "sscan_fwd_zoh.hip", "sscan_device.h", "sscan_internal.h")]
 
@@ -74,20 +75,32 @@ def summarize_counters(fetch_csv: str, write_csv: str) -> dict:
     import csv
 
     def per_kernel(path, counter):
+        # average reading per kernel name; the calibration copy shares its kernel with
+        # other small elementwise launches, so it is keyed by name and grid size
         acc = {}
         with open(path) as f:
             for r in csv.DictReader(f):
                 if r["Counter_Name"] == counter:
-                    acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+                    name = r["Kernel_Name"]
+                    if "AUnaryFunctor" in name:
+                        name = "%s grid=%s" % (name, r["Grid_Size"])
+                    acc.setdefault(name, []).append(float(r["Counter_Value"]))
         return {k: sum(v) / len(v) for k, v in acc.items()}
 
     fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
-    pick = lambda tab, key: next(v for k, v in tab.items() if key in k)
-    # the zero-order-hold forward kernel: its last template argument (EULER) is false
-    zoh = lambda k: "sscan::fwd_kernel<" in k and k.split("(")[0].endswith("false>")
-    copy_bytes = 512 * 1024 * 1024
-    ff = copy_bytes / (pick(fetch, "AUnaryFunctor") * 1024)
-    fw = copy_bytes / (pick(write, "AUnaryFunctor") * 1024)
+    # the 512 MiB copy: 2^27 floats, four per thread
+    calib = " grid=%d" % (COPY_ELEMS // 4)
+    pick = lambda tab: next(v for k, v in tab.items() if "AUnaryFunctor" in k and k.endswith(calib))
+    # the forward kernel in its output mode (4th template argument 0) with the
+    # zero-order hold and no convolution prologue (last two arguments false)
+    def zoh(k):
+        if "sscan::fwd_kernel<" not in k:
+            return False
+        args = [a.strip() for a in k.split("(")[0].split("<", 1)[1].rstrip(">").split(",")]
+        return args[3] == "0" and args[-2:] == ["false", "false"]
+    copy_bytes = COPY_ELEMS * 4
+    ff = copy_bytes / (pick(fetch) * 1024)
+    fw = copy_bytes / (pick(write) * 1024)
     fk = next(v for k, v in fetch.items() if zoh(k))
     wk = next(v for k, v in write.items() if zoh(k))
     rd, wr = fk * 1024 * ff, wk * 1024 * fw
@@ -98,8 +111,8 @@ def summarize_counters(fetch_csv: str, write_csv: str) -> dict:
             "kernel_source_hash": kernel_source_hash(),
             "fetch_size_kib_per_dispatch": round(fk, 1), "write_size_kib_per_dispatch": round(wk, 1),
             "copy_calibration": {"kernel": "torch elementwise mul by 1, 512 MiB fp32 in -> 512 MiB out",
-                                 "fetch_size_kib": round(pick(fetch, "AUnaryFunctor"), 1),
-                                 "write_size_kib": round(pick(write, "AUnaryFunctor"), 1),
+                                 "fetch_size_kib": round(pick(fetch), 1),
+                                 "write_size_kib": round(pick(write), 1),
                                  "fetch_factor": round(ff, 4), "write_factor": round(fw, 4)},
             "hbm_read_bytes_per_launch": int(round(rd)), "hbm_write_bytes_per_launch": int(round(wr)),
             "hbm_bytes_per_launch": int(round(rd + wr)), "algorithmic_bytes_per_launch": alg,
@@ -369,7 +382,7 @@ def main():
                   "timing": f"HIP graph of {per_graph} steps replayed {reps} times"}
 
     if args.copy_calibration:
-        src = torch.ones(128 << 20, dtype=torch.float32, device=dev)  # 512 MiB
+        src = torch.ones(COPY_ELEMS, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
             torch.mul(src, 1.0, out=dst)

@@ -88,15 +88,30 @@ int64_t pick_segments(int64_t base, int64_t seqlen, int64_t per_round, int64_t m
   return best;
 }
 
-// Forward: the main pass runs one 16-wave workgroup per CU (its LDS use).
-int auto_segments(int64_t batch, int64_t seqlen, int64_t dim) {
-  const int64_t ndt = (dim + sscan::kTile - 1) / sscan::kTile;
-  return static_cast<int>(pick_segments(ndt * batch, seqlen, device_cus(), 4 * sscan::kChunk));
+// Segments of the forward.  A grid of at least one workgroup per CU runs unsplit.  A
+// smaller one is split, and its main pass then runs two states per wave, whose LDS use
+// lets two workgroups share a CU, so the split aims at rounds of 2 x CUs workgroups.
+// The checkpoint pass of the backward keeps one state per wave and one-per-CU rounds.
+// Output-mode segments are at least 8 chunks long: with 4-chunk segments the pipeline
+// fill of each segment outweighed the fuller last round (mamba130m layer, 48
+// workgroups: 16 segments 0.094 ms, 32 segments 0.099 ms).
+int auto_segments(int64_t batch, int64_t seqlen, int64_t dim, int mode) {
+  const int64_t base = (dim + sscan::kTile - 1) / sscan::kTile * batch;
+  const int64_t cus = device_cus();
+  if (base >= cus) return 1;
+  const bool out = mode == sscan::kFwdOut;
+  return static_cast<int>(pick_segments(base, seqlen, (out ? 2 : 1) * cus, (out ? 8 : 4) * sscan::kChunk));
 }
 
+// States per wave of a forward launch of nwg workgroups: two once there are more
+// workgroups than CUs (so a CU can hold two), one otherwise.  Measured on the
+// 256-workgroup training shape: one state per wave 0.476 ms, two 0.556 ms; on split
+// shapes two states per wave won (long context 3.45 -> 2.69 ms).
+int fwd_states_per_wave(int64_t N, int64_t nwg) { return (N >= 3 && nwg > device_cus()) ? 2 : 1; }
+
 SegPlan plan_segments(int64_t batch, int64_t seqlen, int64_t dim, int64_t N, int64_t requested,
-                      size_t ws_bytes, bool have_ws) {
-  int64_t want = requested > 0 ? requested : auto_segments(batch, seqlen, dim);
+                      size_t ws_bytes, bool have_ws, int mode = sscan::kFwdOut) {
+  int64_t want = requested > 0 ? requested : auto_segments(batch, seqlen, dim, mode);
   const int64_t maxseg = (seqlen + sscan::kChunk - 1) / sscan::kChunk;
   if (want > maxseg) want = maxseg;
   if (want < 1) want = 1;
@@ -234,6 +249,7 @@ int fwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dty
   p.batch = batch; p.L = seqlen; p.dim = dim; p.N = static_cast<int>(N);
   p.ndtiles = (dim + sscan::kTile - 1) / sscan::kTile;
   p.seg_len = pl.seg_len; p.nseg = pl.nseg;
+  p.npw = fwd_states_per_wave(N, p.ndtiles * batch * pl.nseg);
   p.euler = (flags & SSCAN_FLAG_EULER) != 0;
   p.conv_w = cv.w; p.conv_b = cv.b; p.conv_s = cv.state_in; p.dconv = static_cast<int>(cv.w ? cv.dconv : 0);
   const bool bf16 = dtype == SSCAN_BF16;
@@ -312,7 +328,7 @@ BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t N) {
   lo.gA = off;   off += round256(static_cast<size_t>(lo.bseg) * bdn * 4);
   lo.gD = off;   off += round256(static_cast<size_t>(lo.bseg) * batch * dim * 4);
   lo.gb = off;   off += round256(static_cast<size_t>(lo.bseg) * batch * dim * 4);
-  const SegPlan pl = plan_segments(batch, seqlen, dim, N, 0, ~size_t(0), true);
+  const SegPlan pl = plan_segments(batch, seqlen, dim, N, 0, ~size_t(0), true, sscan::kFwdCkpt);
   lo.nseg = pl.nseg;
   lo.seg_len = pl.seg_len;
   lo.seg = off;  off += round256(seg_workspace_bytes(batch, dim, N, pl.nseg));
@@ -398,6 +414,7 @@ int bwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dty
   p.batch = batch; p.L = seqlen; p.dim = dim; p.N = static_cast<int>(N);
   p.ndtiles = ndt; p.nblk = nblk;
   p.seg_len = lo.seg_len; p.nseg = lo.nseg;
+  p.npw = 1;
   p.euler = euler;
   p.ckpt = ckpt;
   hipError_t e;

@@ -17,11 +17,12 @@
 // dphi/dA = (Delta Abar - phi)/A, evaluated by its Taylor series in u = Delta A when
 // |u| < 0.5), Delta for the Euler rule (dphi/dDelta = 1, dphi/dA = 0).
 //
-// Work decomposition: a workgroup owns (batch row, 64-channel tile); lane =
-// channel, and each wave owns four states (a wave's sums over its states are
-// formed in registers, so only one partial per wave crosses LDS).  A checkpoint pass of the
-// forward kernel has stored the state entering every 16-step block.  The workgroup
-// walks the blocks from last to first; per block:
+// Work decomposition: a workgroup owns (batch row, 64-channel tile, reverse
+// segment); lane = channel, and each wave owns kBwdSpw (two) states (a wave's sums
+// over its states are formed in registers, so only one partial per wave crosses
+// LDS).  A checkpoint pass of the forward kernel has stored the state entering
+// every kBwdBlock-step (8-step) block.  The workgroup walks its blocks from last to
+// first, with each block's global inputs loaded one block ahead; per block:
 //   P1  each wave loads its timesteps' x, dt, z, dy; Delta, x and gyo are staged to
 //       LDS, with the block's B and C rows;
 //   P2  each wave recomputes its state over the block from the checkpoint (the
@@ -203,7 +204,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(
   const float bias2 = biasg ? biasg[dd] * kLog2e : 0.f;
   const float dsk = Dg ? Dg[dd] : 0.f;
 
-  // this wave's states n0 .. n0 + 3; phantom states (n >= N) get A = 0 and stay
+  // this wave's states n0 .. n0 + S - 1; phantom states (n >= N) get A = 0 and stay
   // out of every output
   const int n0 = S * w;
   // gradient entering the end of this segment ([batch][dim][N] slice): the carry of

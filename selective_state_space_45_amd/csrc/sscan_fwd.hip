@@ -45,10 +45,12 @@ __global__ __launch_bounds__(256) void fill_state_kernel(float* __restrict__ dst
   if (i < n) dst[i] = src ? src[i] : 0.f;
 }
 
-// One state per wave: N rounded up to a power of two waves (at most 16).
-int fwd_nsplit(int N) {
+// Waves per workgroup: N / (states per wave) rounded up to a power of two (at most 16).
+int fwd_nsplit(int npw, int N) {
+  const int per = (npw == 2 && N >= 3) ? 2 : 1;
+  const int need = (N + per - 1) / per;
   int ns = 1;
-  while (ns < N) ns <<= 1;
+  while (ns < need) ns <<= 1;
   return ns;
 }
 

@@ -6,10 +6,11 @@
 // h_l = Abar h_{l-1} + Bbar x_l, y_l = (C_l . h_l + D x_l) * silu(z_l).
 //
 // Work decomposition.  A workgroup owns one (batch row, 64-channel tile, sequence
-// segment).  Its NSPLIT waves split the N states, one state per wave (NSPLIT is N
-// rounded up to a power of two), so the whole state of a channel stays in
-// registers but spread over waves, and each lane of a wave is one channel.  The sequence is consumed in chunks of kChunk
-// timesteps, software-pipelined with one barrier per chunk:
+// segment).  Its NSPLIT waves split the N states, NPW (one or two) states per wave
+// (NSPLIT is N / NPW rounded up to a power of two), so the whole state of a channel
+// stays in registers but spread over waves, and each lane of a wave is one channel.
+// The sequence is consumed in chunks of kChunk timesteps, software-pipelined with one
+// barrier per chunk:
 //   prologue   x, dt, z loaded coalesced along channels (each (l, d) once per
 //              workgroup), Delta*log2(e) and x staged to LDS, silu(z) and D*x
 //              kept in registers for the epilogue;
@@ -18,7 +19,10 @@
 //              state after every timestep is written to LDS;
 //   epilogue   each wave reads back all N states of its own prologue timesteps,
 //              forms C.h with the C row (scalar loads), adds the skip term,
-//              applies the gate and stores y coalesced.
+//              applies the gate and stores y coalesced.  With two states per wave
+//              the recurrence forms each wave's share of C.h instead (C through
+//              scalar loads like B) and the epilogue adds NSPLIT partials; the
+//              staging then fits two workgroups in a CU's LDS.
 // The state update uses h <- Abar (h + k) - k with k = x B / A, which equals
 // Abar h + (Abar - 1) B x / A = Abar h + Bbar x: one add and one fma per state.
 // A wave whose channels have some A == 0 switches to the explicit form with the
@@ -53,6 +57,11 @@ struct BRaw {
     for (int j = 0; j < NPW; ++j) v[j] = B[row + joff[j]];
   }
   __device__ __forceinline__ float get(int j, int) const { return to_f32(v[j]); }
+  __device__ __forceinline__ void clear_missing(const bool* have) {
+#pragma unroll
+    for (int j = 0; j < NPW; ++j)
+      if (!have[j]) v[j] = Tin(0);
+  }
 };
 
 template <int NPW>
@@ -66,6 +75,8 @@ struct BRaw<bf16_t, true, NPW> {
     if constexpr (NPW == 2) return __uint_as_float(j == 0 ? (wd << 16) : (wd & 0xffff0000u));
     return __uint_as_float((wd >> sel) << 16);
   }
+  // N is even here, so a wave's two states are both real or both past N.
+  __device__ __forceinline__ void clear_missing(const bool*) {}
 };
 
 // C row of one timestep (all N states) as float32, read through scalar loads.
@@ -145,9 +156,15 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
   __shared__ float s_d2[2][T][kTile];
   __shared__ float s_xv[2][T][kTile];
   // States after each timestep, for the readout C.h done by the epilogue wave.
+  // PART (output mode, two states per wave): each wave forms its own share of C.h in
+  // the recurrence, so one partial per wave and timestep crosses LDS instead of one
+  // state per state index; that halves this buffer and lets two workgroups share a CU.
   constexpr int NS = NSPLIT * NPW;
-  __shared__ float s_h[OUT ? 2 : 1][OUT ? NS : 1][T][kTile];
-  __shared__ float s_red[AGG ? NSPLIT : 1][kTile];
+  constexpr bool PART = OUT && NPW == 2;
+  __shared__ float s_h[OUT ? 2 : 1][OUT ? (PART ? NSPLIT : NS) : 1][T][kTile];
+  // AGG: per-wave sums of Delta, in the state buffer (unused in that mode)
+  static_assert(NSPLIT <= T, "s_red fits in s_h[0][0]");
+  float (*s_red)[kTile] = s_h[0][0];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -207,6 +224,8 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
   const Tin* __restrict__ Bw = Bg + (b * L + l_begin) * N + nbase;
   // C rows of the segment (the epilogue reads whole rows).
   const Tin* __restrict__ Cs = Cg + (b * L + l_begin) * N;
+  // PART: C of this wave's states, addressed like B.
+  const Tin* __restrict__ Cw = Cg + (b * L + l_begin) * N + nbase;
 
   float h[NPW];
 #pragma unroll
@@ -236,6 +255,7 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
   float eg[2][TPW], ed[2][TPW];
   float ssum = 0.f, scomp = 0.f;
   BRaw<Tin, PAIR, NPW> bc[T];
+  BRaw<Tin, PAIR, NPW> cc[PART ? T : 1];
 
   // Global loads of x, dt, z for this wave's prologue timesteps of chunk c.
   auto gload = [&](int c) {
@@ -280,6 +300,14 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
     const Tin* Bc = Bw + off;
 #pragma unroll
     for (int t = HH * H; t < (HH + 1) * H; ++t) bc[t].load(Bc, t * N, joff);
+    if constexpr (PART) {
+      const Tin* Cc = Cw + off;
+#pragma unroll
+      for (int t = HH * H; t < (HH + 1) * H; ++t) {
+        cc[t].load(Cc, t * N, joff);
+        cc[t].clear_missing(have);
+      }
+    }
   };
   // The same for the last, partial chunk: timesteps past the segment end read the
   // last row of the segment (they are identity steps whatever B holds).
@@ -290,6 +318,14 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
     const Tin* Bc = Bw + off;
 #pragma unroll
     for (int t = 0; t < T; ++t) bc[t].load(Bc, static_cast<int64_t>(lc + (t < last ? t : last)) * N, joff);
+    if constexpr (PART) {
+      const Tin* Cc = Cw + off;
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        cc[t].load(Cc, static_cast<int64_t>(lc + (t < last ? t : last)) * N, joff);
+        cc[t].clear_missing(have);
+      }
+    }
   };
 
   auto prologue = [&](auto pc, int c) {
@@ -332,6 +368,12 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
     }
   };
 
+  // PART: this wave's share of C.h after timestep t, to LDS for the epilogue.
+  auto stage = [&](auto pc, int t) {
+    constexpr int P = decltype(pc)::value;
+    if constexpr (PART) s_h[P][w][t][lane] = fmaf(cc[t].get(1, sel), h[1], cc[t].get(0, sel) * h[0]);
+  };
+
   // One timestep of this wave's states, staged to LDS for the readout.  Fast form:
   // h <- Abar (h + k) - k with k = x B / A.  Safe form (a wave with some A == 0):
   // h <- Abar h + g B x with g = (Abar - 1)/A, or Delta when A == 0.
@@ -345,8 +387,9 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
 #pragma unroll
         for (int j = 0; j < NPW; ++j) {
           h[j] = fmaf(ea[t][j], h[j], vx[t].y * bc[t].get(j, sel));
-          if constexpr (OUT) s_h[P][n0 + j][t][lane] = h[j];
+          if constexpr (OUT && !PART) s_h[P][n0 + j][t][lane] = h[j];
         }
+        stage(pc, t);
       }
     } else if (!zeroA) {
 #pragma unroll
@@ -356,8 +399,9 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
           const float q = bc[t].get(j, sel) * iAj[j];
           const float k = vx[t].y * q;
           h[j] = fmaf(ea[t][j], h[j] + k, -k);
-          if constexpr (OUT) s_h[P][n0 + j][t][lane] = h[j];
+          if constexpr (OUT && !PART) s_h[P][n0 + j][t][lane] = h[j];
         }
+        stage(pc, t);
       }
     } else {
 #pragma unroll
@@ -367,8 +411,9 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
         for (int j = 0; j < NPW; ++j) {
           const float g = live[j] * ((Aj[j] != 0.f) ? (ea[t][j] - 1.f) * iAj[j] : dl);
           h[j] = fmaf(ea[t][j], h[j], g * bc[t].get(j, sel) * vx[t].y);
-          if constexpr (OUT) s_h[P][n0 + j][t][lane] = h[j];
+          if constexpr (OUT && !PART) s_h[P][n0 + j][t][lane] = h[j];
         }
+        stage(pc, t);
       }
     }
   };
@@ -384,14 +429,23 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
         const int t = w + NSPLIT * i;
         const int l = c * T + t;
         if (l < seg_n) {
-          float hv[NS], cv[NS];
-#pragma unroll
-          for (int n = 0; n < NS; ++n) hv[n] = s_h[P][n][t][lane];
-          load_c_row<Tin, PAIR, NS>(Cs + static_cast<int64_t>(l) * N, N, cv);
           float sacc = dx[i];
+          if constexpr (PART) {
+            float pv[NSPLIT];
 #pragma unroll
-          for (int n = 0; n < NS; ++n)
-            if (n < N) sacc = fmaf(cv[n], hv[n], sacc);
+            for (int q = 0; q < NSPLIT; ++q) pv[q] = s_h[P][q][t][lane];
+#pragma unroll
+            for (int q = 0; q < NSPLIT; ++q)
+              if (NPW * q < N) sacc += pv[q];
+          } else {
+            float hv[NS], cv[NS];
+#pragma unroll
+            for (int n = 0; n < NS; ++n) hv[n] = s_h[P][n][t][lane];
+            load_c_row<Tin, PAIR, NS>(Cs + static_cast<int64_t>(l) * N, N, cv);
+#pragma unroll
+            for (int n = 0; n < NS; ++n)
+              if (n < N) sacc = fmaf(cv[n], hv[n], sacc);
+          }
           if (dvalid) store_val(&(Yb + static_cast<int64_t>(l) * dim)[lane], sacc * g[i]);
         }
       }
@@ -517,10 +571,10 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
   }
 }
 
-template <typename Tin, int NS, int MODE, bool PR, int NF, bool EU, bool CV>
+template <typename Tin, int NS, int NPW, int MODE, bool PR, int NF, bool EU, bool CV>
 void launch_one(const FwdParams& p, dim3 grid, hipStream_t s) {
   FwdShape sh{p.batch, p.L, p.dim, p.seg_len, p.ndtiles, p.nblk, p.N, p.nseg, p.dconv};
-  hipLaunchKernelGGL((fwd_kernel<Tin, NS, 1, MODE, PR, NF, EU, CV>), grid, dim3(NS * 64), 0, s,
+  hipLaunchKernelGGL((fwd_kernel<Tin, NS, NPW, MODE, PR, NF, EU, CV>), grid, dim3(NS * 64), 0, s,
                      static_cast<const Tin*>(p.x), static_cast<const Tin*>(p.dt), static_cast<const Tin*>(p.z),
                      static_cast<const Tin*>(p.B), static_cast<const Tin*>(p.C), p.A, p.Dskip, p.bias, p.h_init,
                      static_cast<Tin*>(p.y), p.h_last, p.agg_h, p.agg_s, p.ckpt, p.conv_w, p.conv_b, p.conv_s, sh);
@@ -528,16 +582,29 @@ void launch_one(const FwdParams& p, dim3 grid, hipStream_t s) {
 
 template <typename Tin, int MODE, bool PR, bool EU, bool CV>
 void launch_by_n(const FwdParams& p, dim3 grid, hipStream_t s) {
-  switch (fwd_nsplit(p.N)) {
-    case 1: launch_one<Tin, 1, MODE, PR, 0, EU, CV>(p, grid, s); break;
-    case 2: launch_one<Tin, 2, MODE, PR, 0, EU, CV>(p, grid, s); break;
-    case 4: launch_one<Tin, 4, MODE, PR, 0, EU, CV>(p, grid, s); break;
-    case 8: launch_one<Tin, 8, MODE, PR, 0, EU, CV>(p, grid, s); break;
+  if (p.npw == 2 && p.N >= 3) {
+    switch (fwd_nsplit(2, p.N)) {
+      case 2: launch_one<Tin, 2, 2, MODE, PR, 0, EU, CV>(p, grid, s); break;
+      case 4: launch_one<Tin, 4, 2, MODE, PR, 0, EU, CV>(p, grid, s); break;
+      default:
+        if (p.N == 16)
+          launch_one<Tin, 8, 2, MODE, PR, 16, EU, CV>(p, grid, s);
+        else
+          launch_one<Tin, 8, 2, MODE, PR, 0, EU, CV>(p, grid, s);
+        break;
+    }
+    return;
+  }
+  switch (fwd_nsplit(1, p.N)) {
+    case 1: launch_one<Tin, 1, 1, MODE, PR, 0, EU, CV>(p, grid, s); break;
+    case 2: launch_one<Tin, 2, 1, MODE, PR, 0, EU, CV>(p, grid, s); break;
+    case 4: launch_one<Tin, 4, 1, MODE, PR, 0, EU, CV>(p, grid, s); break;
+    case 8: launch_one<Tin, 8, 1, MODE, PR, 0, EU, CV>(p, grid, s); break;
     default:
       if (p.N == 16)
-        launch_one<Tin, 16, MODE, PR, 16, EU, CV>(p, grid, s);
+        launch_one<Tin, 16, 1, MODE, PR, 16, EU, CV>(p, grid, s);
       else
-        launch_one<Tin, 16, MODE, PR, 0, EU, CV>(p, grid, s);
+        launch_one<Tin, 16, 1, MODE, PR, 0, EU, CV>(p, grid, s);
       break;
   }
 }

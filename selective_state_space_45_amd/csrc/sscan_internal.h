@@ -41,6 +41,8 @@ struct FwdParams {
   int64_t ndtiles;        // ceil(dim / kTile)
   int N;
   int nseg;
+  int npw;                // states per wave: 1, or 2 (N >= 3; the output mode then stages one
+                          // C.h partial per wave, and two workgroups share a CU)
   bool euler;             // Bbar = Delta * B instead of the zero-order hold
 };
 
@@ -116,8 +118,8 @@ struct BwdShape {
 
 hipError_t launch_bwd(const BwdParams& p, bool bf16, hipStream_t s);
 
-// Waves per workgroup of the forward kernels for a given N (each wave owns one state).
-int fwd_nsplit(int N);
+// Waves per workgroup of the forward kernel with npw states per wave.
+int fwd_nsplit(int npw, int N);
 
 // Launchers; return hipSuccess or the launch error.
 hipError_t launch_fwd_main(const FwdParams& p, bool bf16, hipStream_t s);

@@ -140,6 +140,10 @@ def test_workspace_size(lib):
     # a long single-row sequence is split: carry + end state + sums per segment
     ws = lib.sscan_fwd_workspace_size(1, 131072, 2560, 16, 1)
     assert ws > 0 and ws % (4 * 2560 * 33) == 0
+    # segment counts by round fill with two workgroups per CU (256 CUs): 40 workgroups
+    # x 64 segments = 5 full rounds of 512; 48 x 16 (segments >= 128 steps)
+    assert ws == 64 * 4 * 2560 * 33
+    assert lib.sscan_fwd_workspace_size(2, 2048, 1536, 16, 0) == 16 * 4 * 2 * 1536 * 33
     assert lib.sscan_fwd_workspace_size(1, 0, 2560, 16, 1) == 0
 
 

@@ -286,6 +286,32 @@ def test_unsupported_dstate_raises(ss):
     assert ei.value.code == 2
 
 
+@pytest.mark.parametrize("N", [4, 6, 16])
+def test_bf16_bc_two_byte_aligned(ss, orc, N):
+    """bf16 B and C whose base addresses are only 2-byte aligned: the kernels then read
+    each state's element on its own instead of in aligned pairs."""
+    import torch
+    w = W.make_scan_inputs(2, 77, 130, N, "bf16", seed=400 + N, name=f"unaligned B/C N={N}")
+    note(f"[case] bf16 B/C at odd element offsets, B=2 L=77 D=130 N={N}")
+
+    def odd_view(a):
+        flat = torch.zeros(a.size + 1, dtype=torch.bfloat16, device="cuda")
+        flat[1:] = tdev(a, "bf16").reshape(-1)
+        v = flat[1:].view(a.shape)
+        assert v.data_ptr() % 4 == 2
+        return v
+
+    x, dt, z = tdev(w.x, "bf16"), tdev(w.dt, "bf16"), tdev(w.z, "bf16")
+    y = torch.full_like(x, float("nan"))
+    st = torch.full((w.batch, w.dim, N), float("nan"), dtype=torch.float32, device="cuda")
+    ss.sscan_fwd(x, dt, f32dev(w.A), odd_view(w.B), odd_view(w.C), D=f32dev(w.D), z=z,
+                 delta_bias=f32dev(w.dt_bias), out=y, last_state=st)
+    torch.cuda.synchronize()
+    yr, sr = run_oracle(orc, w)
+    assert_close(host(y), yr, TAU["bf16"], "y")
+    assert_close(host(st), sr, TAU["bf16"], "last_state")
+
+
 # ----------------------------------------------------------------------------
 # single-token step
 # ----------------------------------------------------------------------------
