@@ -151,10 +151,11 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
   static_assert(T % NSPLIT == 0, "chunk must split evenly over waves");
   static_assert(NPW == 1 || NPW == 2, "one or two states per wave");
 
-  // Delta*log2(e) and x (Delta*x for EULER) of each staged timestep, as two 32-bit
-  // arrays (32-bit LDS reads run at about twice the rate of 64-bit ones here).
-  __shared__ float s_d2[2][T][kTile];
-  __shared__ float s_xv[2][T][kTile];
+  // (Delta*log2(e), x) of each staged timestep (Delta*x instead of x for EULER),
+  // interleaved so a lane reads both with one 64-bit access: on the training shape
+  // that ran 2 % faster than two separate 32-bit arrays, whose extra read instructions
+  // cost more than the wider accesses.
+  __shared__ float2 s_dx[2][T][kTile];
   // States after each timestep, for the readout C.h done by the epilogue wave.
   // PART (output mode, two states per wave): each wave forms its own share of C.h in
   // the recurrence, so one partial per wave and timestep crosses LDS instead of one
@@ -354,8 +355,7 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
       }
       float d2 = softplus_log2e(fmaf(to_f32(rdt[i]), kLog2e, bias2));
       d2 = lv ? d2 : 0.f;  // a padded step is the identity: Delta = 0, x = 0
-      s_d2[P][t][lane] = d2;
-      s_xv[P][t][lane] = EULER ? (d2 * kLn2) * xv : xv;
+      s_dx[P][t][lane] = make_float2(d2, EULER ? (d2 * kLn2) * xv : xv);
       if constexpr (AGG) {
         const float yk = d2 - scomp;
         const float tk = ssum + yk;
@@ -454,11 +454,9 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
   auto read_dx = [&](auto pc, float2* vx) {
     constexpr int P = decltype(pc)::value;
 #pragma unroll
-    for (int t = 0; t < T; ++t) vx[t].x = s_d2[P][t][lane];
-#pragma unroll
-    for (int t = 0; t < T - 1; ++t) vx[t].y = s_xv[P][t][lane];
+    for (int t = 0; t < T - 1; ++t) vx[t] = s_dx[P][t][lane];
     __builtin_amdgcn_sched_barrier(0);
-    vx[T - 1].y = s_xv[P][T - 1][lane];  // issued last: once it has arrived, all have
+    vx[T - 1] = s_dx[P][T - 1][lane];  // issued last: once it has arrived, all have
     __builtin_amdgcn_sched_barrier(0);
   };
 
