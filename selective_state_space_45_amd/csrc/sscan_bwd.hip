@@ -324,7 +324,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(
 
     // ---- P2: recompute the block's states from the checkpoint; partial C.h of the
     // readout to LDS; terms of dC summed across lanes ----
-    float hist[S][T];
+    float hist[S][T];   // state entering each step
+    float ahist[S][T];  // Abar of each step, reused by the reverse recurrence
     {
       float red[S * T];
       auto recompute = [&](auto safe) {
@@ -341,6 +342,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(
 #pragma unroll
           for (int q = 0; q < S; ++q) {
             const float a = hw_exp2(d2 * An[q]);
+            ahist[q][t] = a;
             hist[q][t] = h[q];
             if constexpr (EULER) {
               h[q] = fmaf(a, h[q], (d2 * kLn2) * xv * bq[q]);
@@ -386,26 +388,35 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(
         float r1 = 0.f, r2 = 0.f;
 #pragma unroll
         for (int q = 0; q < S; ++q) {
-          const float a = hw_exp2(d2 * An[q]);
+          const float a = ahist[q][t];
           const float hp = hist[q][t];
           const float gh = fmaf(go, cq[q], G[q]);
           const float bx = bq[q] * xv;
-          float phi;
+          // hn = h_l, the state after the step: h_l = Abar h_{l-1} + phi B x
+          const float hn = (t + 1 < T) ? hist[q][t + 1] : h[q];
+          float gphi, Gn;
           if constexpr (EULER) {
-            phi = delta;
+            gphi = gh * delta;
+            Gn = a * gh;
             r2 = fmaf(gh, fmaf(An[q] * a, hp, bx), r2);
             gA[q] = fmaf(gh, delta * a * hp, gA[q]);
           } else if (!zeroA) {
-            // d h / d A = Delta Abar (h_{l-1} + k) - phi k with k = B x / A: the term
-            // (Delta Abar - phi) k cancels for small Delta A, but only down to a few
-            // ulp of Delta Abar k, the size of the leading term Delta Abar h_{l-1}
-            phi = (a - 1.f) * iAn[q];
-            r2 = fmaf(gh * a, fmaf(An[q], hp, bx), r2);
+            // d h_l / d Delta = Abar (A h_{l-1} + B x) = A hn + B x, and
+            // d h_l / d A = Delta Abar (h_{l-1} + k) - phi k = Delta (hn + k) - phi k
+            // with k = B x / A; gh phi = (Abar gh - gh) / A, so phi is never formed.
+            // The term (Delta Abar - phi) k cancels for small Delta A, but only down to
+            // a few ulp of Delta k, the size of the leading term
+            Gn = a * gh;
+            gphi = (Gn - gh) * iAn[q];
+            r2 = fmaf(gh, fmaf(An[q], hn, bx), r2);
             const float k = bx * iAn[q];
-            gA[q] = fmaf(gh, fmaf(delta * a, hp + k, -phi * k), gA[q]);
+            gA[q] = fmaf(delta, gh * (hn + k), gA[q]);
+            gA[q] = fmaf(-gphi, k, gA[q]);
           } else {
-            phi = (An[q] != 0.f) ? (a - 1.f) * iAn[q] : delta;
-            r2 = fmaf(gh * a, fmaf(An[q], hp, bx), r2);
+            const float phi = (An[q] != 0.f) ? (a - 1.f) * iAn[q] : delta;
+            gphi = gh * phi;
+            Gn = a * gh;
+            r2 = fmaf(gh, fmaf(An[q], hn, bx), r2);
             // a wave with some A == 0: dphi/dA = Delta^2 (u e^u - e^u + 1)/u^2, u = Delta A,
             // from its series for |u| < 0.5 and its closed form otherwise; both are
             // computed (each finite everywhere) and blended, so no per-lane branch
@@ -417,10 +428,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(
             const float dphi_dA = fmaf(wsel, ser - dir, dir);
             gA[q] = fmaf(gh, fmaf(delta * a, hp, dphi_dA * bx), gA[q]);
           }
-          const float gphi = gh * phi;
           red[q * T + t] = gphi * xv;
           r1 = fmaf(gphi, bq[q], r1);
-          G[q] = a * gh;
+          G[q] = Gn;
         }
         s_r1[w][t][lane] = r1;
         s_r2[w][t][lane] = r2;
