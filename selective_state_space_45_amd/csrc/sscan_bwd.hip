@@ -510,22 +510,26 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(
 // reverse recurrence G <- Abar (gyo C + G) run over the segment from G = 0 at its end
 // gives the gradient its steps send to the state before its start (ragg_g); with the
 // segment's sum of Delta*log2(e) (ragg_s), exp2(A * sum) is the product of Abar over
-// it.  A workgroup per (batch row, channel tile, segment); one state per wave (this
-// pass needs few registers, so it takes the wide layout for occupancy), blocks of
-// kAggBlock steps staged through LDS.
+// it.  A workgroup per (batch row, channel tile, segment) with AS states per wave;
+// blocks of kAggBlock steps staged through LDS, double-buffered so that the staging
+// of the next block overlaps the steps of this one, with one barrier per block.
 constexpr int kAggBlock = 32;
 
-template <typename Tin, int NW, int NFIX>
+template <typename Tin, int NW, int AS, int NFIX>
 __global__ __launch_bounds__(NW * 64) void bwd_agg_kernel(
     const Tin* __restrict__ dtg, const Tin* __restrict__ zg, const Tin* __restrict__ Cg,
     const Tin* __restrict__ dyg, const float* __restrict__ Ag, const float* __restrict__ biasg,
     float* __restrict__ ragg_g, float* __restrict__ ragg_s, BwdShape sh) {
   constexpr int T = kAggBlock;
+  constexpr int NSP = NW * AS;   // states covered (N rounded up)
   constexpr int TPW = T / NW;
   static_assert(T % NW == 0, "block must split evenly over waves");
-  __shared__ float s_d2[T][kTile];
-  __shared__ float s_go[T][kTile];
-  __shared__ float s_C[NW][T];
+  static_assert(AS == 1 || AS == 2, "one or two states per wave");
+  static_assert(T * NSP <= NW * 64, "one thread per staged C element");
+  // (Delta * log2(e), gyo) of each staged timestep; C of each state (pairs for AS = 2)
+  __shared__ float2 s_dg[2][T][kTile];
+  __shared__ float s_C[2][T][NSP];
+  __shared__ float s_sum[NW][kTile];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -544,10 +548,16 @@ __global__ __launch_bounds__(NW * 64) void bwd_agg_kernel(
   const int64_t dd = dvalid ? d : dim - 1;
   const bool hasZ = zg != nullptr;
   const float bias2 = biasg ? biasg[dd] * kLog2e : 0.f;
-  const int n = w;   // phantom states (n >= N) have A = 0, C = 0 and are not written
-  const float An = (n < N) ? Ag[dd * N + n] : 0.f;
-  float G = 0.f;
-  float ssum = 0.f, scomp = 0.f;
+  // this wave's states n0 .. n0 + AS - 1; phantom states (n >= N) have A = 0, C = 0
+  // and are not written
+  const int n0 = AS * w;
+  float An[AS], G[AS];
+#pragma unroll
+  for (int q = 0; q < AS; ++q) {
+    An[q] = (n0 + q < N) ? Ag[dd * N + n0 + q] : 0.f;
+    G[q] = 0.f;
+  }
+  float ssum = 0.f, scomp = 0.f;   // Kahan sum of this wave's staged Delta*log2(e)
 
   const int64_t l_beg = static_cast<int64_t>(seg) * sh.seg_blocks * kBwdBlock;
   const int64_t l_end = (l_beg + sh.seg_blocks * kBwdBlock < L) ? l_beg + sh.seg_blocks * kBwdBlock : L;
@@ -556,8 +566,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_agg_kernel(
   // inputs of one block, loaded one block ahead of their use
   Tin r_dt[TPW], r_z[TPW], r_dy[TPW];
   Tin r_c = Tin(0);
-  const int c_n = tid / T, c_t = tid - (tid / T) * T;   // C element this thread stages
-  const bool c_stager = tid < T * NW;                    // [NW][T] elements, half the threads
+  const int c_t = tid / NSP, c_n = tid - (tid / NSP) * NSP;   // C element this thread stages
+  const bool c_stager = tid < T * NSP;
   auto gload = [&](int64_t c) {
     const int64_t l0 = l_beg + c * T;
     const int cnt = static_cast<int>((l_end - l0) < T ? (l_end - l0) : T);
@@ -578,7 +588,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_agg_kernel(
     }
     r_c = (c_stager && c_n < N && c_t < cnt) ? Cg[(b * L + l0 + c_t) * N + c_n] : Tin(0);
   };
-  auto prologue = [&](int64_t c) {
+  auto prologue = [&](int64_t c, int buf) {
     const int64_t l0 = l_beg + c * T;
     const int cnt = static_cast<int>((l_end - l0) < T ? (l_end - l0) : T);
 #pragma unroll
@@ -587,33 +597,48 @@ __global__ __launch_bounds__(NW * 64) void bwd_agg_kernel(
       const float zv = to_f32(r_z[i]), gy = to_f32(r_dy[i]);
       float go = gy;
       if (hasZ) go = gy * (zv * hw_rcp(1.f + hw_exp2(-zv * kLog2e)));
-      s_d2[t][lane] = (t < cnt) ? softplus_log2e(fmaf(to_f32(r_dt[i]), kLog2e, bias2)) : 0.f;
-      s_go[t][lane] = go;
+      const float d2 = (t < cnt) ? softplus_log2e(fmaf(to_f32(r_dt[i]), kLog2e, bias2)) : 0.f;
+      s_dg[buf][t][lane] = make_float2(d2, go);
+      const float yk = d2 - scomp;   // padded steps add 0
+      const float tk = ssum + yk;
+      scomp = (tk - ssum) - yk;
+      ssum = tk;
     }
-    if (c_stager) s_C[c_n][c_t] = to_f32(r_c);
+    if (c_stager) s_C[buf][c_t][c_n] = to_f32(r_c);
   };
-  if (nb > 0) gload(nb - 1);
+  if (nb > 0) {
+    gload(nb - 1);
+    prologue(nb - 1, static_cast<int>((nb - 1) & 1));
+    if (nb > 1) gload(nb - 2);
+  }
   for (int64_t c = nb - 1; c >= 0; --c) {
-    prologue(c);
-    if (c > 0) gload(c - 1);
+    const int buf = static_cast<int>(c & 1);
+    // block c is staged, and every wave is done with the other buffer (block c + 1)
     __syncthreads();
+    if (c > 0) {
+      prologue(c - 1, buf ^ 1);
+      if (c > 1) gload(c - 2);
+    }
 #pragma unroll 8
     for (int t = T - 1; t >= 0; --t) {
-      const float d2 = s_d2[t][lane];
-      G = hw_exp2(d2 * An) * fmaf(s_go[t][lane], s_C[n][t], G);
-      if (w == 0) {   // Kahan sum of Delta*log2(e) (padded steps add 0)
-        const float yk = d2 - scomp;
-        const float tk = ssum + yk;
-        scomp = (tk - ssum) - yk;
-        ssum = tk;
-      }
+      const float2 dg = s_dg[buf][t][lane];
+#pragma unroll
+      for (int q = 0; q < AS; ++q) G[q] = hw_exp2(dg.x * An[q]) * fmaf(dg.y, s_C[buf][t][n0 + q], G[q]);
     }
-    __syncthreads();
   }
+  s_sum[w][lane] = ssum;
+  __syncthreads();
   if (dvalid) {
     const int64_t row = (static_cast<int64_t>(seg) * sh.batch + b) * dim + d;
-    if (n < N) ragg_g[row * N + n] = G;
-    if (w == 0) ragg_s[row] = ssum;
+#pragma unroll
+    for (int q = 0; q < AS; ++q)
+      if (n0 + q < N) ragg_g[row * N + n0 + q] = G[q];
+    if (w == 0) {
+      float sum = 0.f;
+#pragma unroll
+      for (int q = 0; q < NW; ++q) sum += s_sum[q][lane];
+      ragg_s[row] = sum;
+    }
   }
 }
 
@@ -690,8 +715,11 @@ template <typename Tin, int NW, int NF, bool EU>
 void launch_bwd_one(const BwdParams& p, hipStream_t s) {
   BwdShape sh{p.batch, p.L, p.dim, p.ndtiles, p.nblk, p.seg_blocks, p.N, p.nseg};
   if (p.nseg > 1) {
-    constexpr int AW = NW * kBwdSpw;   // one state per wave in the aggregate pass
-    hipLaunchKernelGGL((bwd_agg_kernel<Tin, AW, NF>), dim3(static_cast<unsigned>(p.ndtiles * p.batch * (p.nseg - 1))),
+    // one state per wave in the aggregate pass: twice the reverse pass's waves, for
+    // occupancy (measured: two states per wave was no faster on the training shape)
+    constexpr int AS = 1;
+    constexpr int AW = NW * kBwdSpw / AS;
+    hipLaunchKernelGGL((bwd_agg_kernel<Tin, AW, AS, NF>), dim3(static_cast<unsigned>(p.ndtiles * p.batch * (p.nseg - 1))),
                        dim3(AW * 64), 0, s, static_cast<const Tin*>(p.dt), static_cast<const Tin*>(p.z),
                        static_cast<const Tin*>(p.C), static_cast<const Tin*>(p.dy), p.A, p.bias, p.ragg_g, p.ragg_s,
                        sh);
