@@ -346,6 +346,32 @@ def main():
                "algorithmic_bytes": bw_bytes, "gbs": round(bw_bytes / (bw_ms * 1e-3) / 1e9, 2),
                "tokens_channels_per_s": round(tokch / (bw_ms * 1e-3), 1)}
 
+        # a training step's scan: the forward saves the state every 8 steps and the
+        # backward starts from those states instead of recomputing them
+        ck = torch.empty(ss.checkpoint_bytes(w.batch, w.seqlen, w.dim, w.dstate) // 4, dtype=torch.float32,
+                         device=dev)
+        ck_ws = torch.empty(ss.bwd_workspace_size(w.batch, w.seqlen, w.dim, w.dstate, torch.bfloat16,
+                                                  checkpointed=True), dtype=torch.uint8, device=dev)
+        y_t = torch.empty_like(x)
+        st_t = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev)
+
+        def step_fwd_ck():
+            ss.sscan_fwd(x, dt, A, B, C, D=D, z=z, delta_bias=bias, out=y_t, last_state=st_t, checkpoints=ck)
+
+        def step_bwd_ck():
+            ss.sscan_bwd(x, dt, A, B, C, gy, D=D, z=z, delta_bias=bias, workspace=ck_ws, out=grads, checkpoints=ck)
+
+        for _ in range(3):
+            step_fwd_ck()
+            step_bwd_ck()
+        torch.cuda.synchronize()
+        fck_ms = timed_launches(step_fwd_ck, max(5, args.steps // 5))
+        bck_ms = timed_launches(step_bwd_ck, max(5, args.steps // 5))
+        bwd["train_step"] = {
+            "op": "sscan_fwd with checkpoints, then sscan_bwd from them (no recompute pass)",
+            "fwd_ms": round(fck_ms, 5), "bwd_ms": round(bck_ms, 5), "ms": round(fck_ms + bck_ms, 5),
+            "vs_fwd_plus_bwd_ms": round(ms_per_step + bw_ms, 5)}
+
     # decode step (sscan_step) on the decode workload, reported alongside.  The steps
     # are captured in a HIP graph and replayed, so host-side launch overhead is not
     # counted (the kernel needs ~25 us, about what one Python-side launch costs).

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define SSCAN_VERSION 400
+#define SSCAN_VERSION 410
 #define SSCAN_MAX_DSTATE 16
 #define SSCAN_MAX_DCONV 4
 
@@ -196,7 +196,7 @@ int sscan_step_conv(int64_t batch, int64_t dim, int64_t dstate, int64_t dconv, i
 /*
  * Workspace bytes sscan_bwd needs for a shape (0 for an empty problem).  The
  * backward pass cannot run without it: it holds the state checkpoints (one per
- * 16 timesteps), per-channel-tile partial sums of dB and dC, per-batch-row
+ * 8 timesteps), per-channel-tile partial sums of dB and dC, per-batch-row
  * partial sums of dA, dD and ddelta_bias, and the sequence-split buffers of the
  * checkpoint pass.  Contents are scratch: nothing is kept between calls.
  */
@@ -247,6 +247,63 @@ int sscan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dt
               void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz,
               float* ddelta_bias, float* dinitial_state, void* workspace, size_t workspace_bytes,
               void* stream);
+
+/*
+ * Saved checkpoints for a training step.  The lengnian.github.io notes ("Part3:
+ * Mamba - A Selective SSM") list recomputation among the means by which the
+ * hardware-aware algorithm keeps intermediate results small; sscan_bwd recomputes
+ * the forward states from scratch.  A training step that runs the forward anyway
+ * can instead keep the state at a coarse grain: sscan_fwd_checkpointed writes the
+ * state entering every block of 8 timesteps (1/8 of the four-dimensional state,
+ * nothing in between), and sscan_bwd_checkpointed starts its reverse pass from
+ * those states instead of running the forward recurrence again.
+ *
+ * Layout: checkpoints[b][j][n][d], float32, j = 0 .. ceil(seqlen / 8) - 1, holding
+ * h_{8j-1}, the state entering timestep 8j (the initial state for j = 0).
+ */
+
+/* Bytes of the checkpoint array for a shape (0 for an empty problem). */
+size_t sscan_checkpoint_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
+
+/*
+ * sscan_fwd that also writes the checkpoints.
+ *   checkpoints      : written; at least sscan_checkpoint_bytes bytes, 4-byte aligned,
+ *                      overlapping no other tensor or the workspace
+ *   checkpoint_bytes : its size in bytes
+ * Other arguments, results and errors: as sscan_fwd (there is no convolution
+ * prologue here: the backward pass does not cover it).  y and last_state equal
+ * sscan_fwd's bit for bit.
+ */
+int sscan_fwd_checkpointed(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+                           unsigned int flags, const void* x, const void* delta, const float* A,
+                           const void* B, const void* C, const float* D, const void* z,
+                           const float* delta_bias, const float* initial_state, void* y,
+                           float* last_state, void* workspace, size_t workspace_bytes,
+                           float* checkpoints, size_t checkpoint_bytes, void* stream);
+
+/* Workspace bytes sscan_bwd_checkpointed needs: sscan_bwd's less the checkpoint array. */
+size_t sscan_bwd_checkpointed_workspace_size(int64_t batch, int64_t seqlen, int64_t dim,
+                                             int64_t dstate, int dtype);
+
+/*
+ * sscan_bwd from checkpoints that sscan_fwd_checkpointed wrote for the same x,
+ * delta, A, B, C, delta_bias, initial_state and flags.  The initial state reaches
+ * the backward pass through checkpoint block 0, so it is not an argument here;
+ * dinitial_state is still produced.
+ *   checkpoints      : read; at least sscan_checkpoint_bytes bytes, 4-byte aligned
+ *   workspace        : at least sscan_bwd_checkpointed_workspace_size bytes
+ * Other arguments, results and errors: as sscan_bwd.  The gradients equal
+ * sscan_bwd's to rounding: sscan_bwd's own recomputation may split the sequence
+ * differently from the forward, which rounds the states differently.
+ */
+int sscan_bwd_checkpointed(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+                           unsigned int flags, const void* x, const void* delta, const float* A,
+                           const void* B, const void* C, const float* D, const void* z,
+                           const float* delta_bias, const float* checkpoints,
+                           size_t checkpoint_bytes, const void* dy, const float* dlast_state,
+                           void* dx, void* ddelta, float* dA, void* dB, void* dC, float* dD,
+                           void* dz, float* ddelta_bias, float* dinitial_state, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

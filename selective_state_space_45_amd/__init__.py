@@ -47,6 +47,15 @@ _lib.sscan_bwd_workspace_size.argtypes = [_I64, _I64, _I64, _I64, ctypes.c_int]
 _lib.sscan_bwd_workspace_size.restype = _SZ
 _lib.sscan_bwd.argtypes = [_I64, _I64, _I64, _I64, ctypes.c_int, _U32] + [_P] * 21 + [_SZ, _P]
 _lib.sscan_bwd.restype = ctypes.c_int
+_lib.sscan_checkpoint_bytes.argtypes = [_I64, _I64, _I64, _I64]
+_lib.sscan_checkpoint_bytes.restype = _SZ
+_lib.sscan_fwd_checkpointed.argtypes = [_I64, _I64, _I64, _I64, ctypes.c_int, _U32] + [_P] * 11 + [_P, _SZ, _P, _SZ, _P]
+_lib.sscan_fwd_checkpointed.restype = ctypes.c_int
+_lib.sscan_bwd_checkpointed_workspace_size.argtypes = [_I64, _I64, _I64, _I64, ctypes.c_int]
+_lib.sscan_bwd_checkpointed_workspace_size.restype = _SZ
+_lib.sscan_bwd_checkpointed.argtypes = ([_I64, _I64, _I64, _I64, ctypes.c_int, _U32] + [_P] * 8 + [_P, _SZ] + [_P] * 11
+                                        + [_P, _SZ, _P])
+_lib.sscan_bwd_checkpointed.restype = ctypes.c_int
 
 SSCAN_F32, SSCAN_BF16 = 0, 1
 SSCAN_FLAG_EULER = 1
@@ -109,13 +118,16 @@ def sscan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Te
               last_state: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
               num_segments: Optional[int] = None, euler: bool = False,
               conv_w: Optional[torch.Tensor] = None, conv_b: Optional[torch.Tensor] = None,
-              conv_state_in: Optional[torch.Tensor] = None, conv_state_out: Optional[torch.Tensor] = None):
+              conv_state_in: Optional[torch.Tensor] = None, conv_state_out: Optional[torch.Tensor] = None,
+              checkpoints: Optional[torch.Tensor] = None):
     """Forward selective scan.  x, delta, z: [batch, seqlen, dim]; B, C: [batch, seqlen, dstate]
     (all float32 or all bfloat16); A: [dim, dstate], D, delta_bias: [dim], initial_state:
     [batch, dim, dstate] (float32).  euler: Bbar = Delta B instead of the zero-order hold.
     conv_w [dim, dconv] (float32): x is the raw input of the fused causal depthwise
     convolution + SiLU prologue (conv_b [dim], conv_state_in / conv_state_out
-    [batch, dim, dconv - 1], float32, optional).  Returns y, or (y, last_state)."""
+    [batch, dim, dconv - 1], float32, optional).  checkpoints (a device buffer of at least
+    ``checkpoint_bytes(...)`` bytes): also save the states that ``sscan_bwd(...,
+    checkpoints=...)`` starts from.  Returns y, or (y, last_state)."""
     if x.dim() != 3:
         raise ValueError("x must be [batch, seqlen, dim]")
     batch, seqlen, dim = x.shape
@@ -165,6 +177,12 @@ def sscan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Te
         cargs = [batch, seqlen, dim, dstate, dconv, dt, flags, _ptr(x), _ptr(conv_w), _ptr(conv_b),
                  _ptr(conv_state_in), _ptr(conv_state_out)] + args[7:]
         _check(_lib.sscan_fwd_conv(*cargs, _stream(x.device)))
+    elif checkpoints is not None:
+        if num_segments is not None:
+            raise ValueError("num_segments is not available with checkpoints")
+        _dev(checkpoints, "checkpoints")
+        _check(_lib.sscan_fwd_checkpointed(*args, _ptr(checkpoints),
+                                           checkpoints.numel() * checkpoints.element_size(), _stream(x.device)))
     elif num_segments is None:
         _check(_lib.sscan_fwd(*args, _stream(x.device)))
     else:
@@ -223,8 +241,17 @@ def sscan_step(state: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, A: tor
     return y
 
 
-def bwd_workspace_size(batch: int, seqlen: int, dim: int, dstate: int, dtype=torch.bfloat16) -> int:
-    return int(_lib.sscan_bwd_workspace_size(batch, seqlen, dim, dstate, _DTYPES[dtype]))
+def bwd_workspace_size(batch: int, seqlen: int, dim: int, dstate: int, dtype=torch.bfloat16,
+                       checkpointed: bool = False) -> int:
+    fn = _lib.sscan_bwd_checkpointed_workspace_size if checkpointed else _lib.sscan_bwd_workspace_size
+    return int(fn(batch, seqlen, dim, dstate, _DTYPES[dtype]))
+
+
+def checkpoint_bytes(batch: int, seqlen: int, dim: int, dstate: int) -> int:
+    """Bytes of the checkpoint buffer for ``sscan_fwd(..., checkpoints=...)`` and
+    ``sscan_bwd(..., checkpoints=...)``: the state entering every 8 timesteps,
+    [batch, ceil(seqlen / 8), dstate, dim] float32."""
+    return int(_lib.sscan_checkpoint_bytes(batch, seqlen, dim, dstate))
 
 
 def sscan_bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
@@ -232,11 +259,15 @@ def sscan_bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Te
               delta_bias: Optional[torch.Tensor] = None, initial_state: Optional[torch.Tensor] = None,
               dlast_state: Optional[torch.Tensor] = None, euler: bool = False,
               want_ddelta_bias: bool = True, want_dinitial_state: bool = True,
-              workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None) -> dict:
+              workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None,
+              checkpoints: Optional[torch.Tensor] = None) -> dict:
     """Backward pass of ``sscan_fwd``: gradients of a scalar loss given dy = dLoss/dy
     (same shape and dtype as x) and optionally dlast_state = dLoss/d(last state).
     Returns a dict with dx, ddelta, dA, dB, dC and, as applicable, dD, dz,
-    ddelta_bias, dinitial_state (``out`` may supply preallocated tensors by name)."""
+    ddelta_bias, dinitial_state (``out`` may supply preallocated tensors by name).
+    checkpoints: the buffer ``sscan_fwd(..., checkpoints=...)`` filled for the same
+    inputs; the forward recurrence is then not run again (initial_state then enters
+    through the checkpoints and is not needed)."""
     if x.dim() != 3:
         raise ValueError("x must be [batch, seqlen, dim]")
     batch, seqlen, dim = x.shape
@@ -275,11 +306,19 @@ def sscan_bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Te
     dz = get("dz", x.shape, x.dtype) if z is not None else None
     dbias = get("ddelta_bias", (dim,), torch.float32) if want_ddelta_bias else None
     dh0 = get("dinitial_state", (batch, dim, dstate), torch.float32) if want_dinitial_state else None
-    need = bwd_workspace_size(batch, seqlen, dim, dstate, x.dtype)
+    need = bwd_workspace_size(batch, seqlen, dim, dstate, x.dtype, checkpointed=checkpoints is not None)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     wbytes = workspace.numel() * workspace.element_size()
     flags = SSCAN_FLAG_EULER if euler else 0
+    if checkpoints is not None:
+        _dev(checkpoints, "checkpoints")
+        _check(_lib.sscan_bwd_checkpointed(
+            batch, seqlen, dim, dstate, _DTYPES[x.dtype], flags, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+            _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(checkpoints), checkpoints.numel() * checkpoints.element_size(),
+            _ptr(dy), _ptr(dlast_state), _ptr(dx), _ptr(ddelta), _ptr(dA), _ptr(dB), _ptr(dC), _ptr(dD), _ptr(dz),
+            _ptr(dbias), _ptr(dh0), _ptr(workspace), wbytes, _stream(dev)))
+        return out
     _check(_lib.sscan_bwd(batch, seqlen, dim, dstate, _DTYPES[x.dtype], flags, _ptr(x), _ptr(delta), _ptr(A),
                           _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(initial_state), _ptr(dy),
                           _ptr(dlast_state), _ptr(dx), _ptr(ddelta), _ptr(dA), _ptr(dB), _ptr(dC), _ptr(dD),

@@ -55,6 +55,12 @@ struct SegPlan {
   int64_t seg_len;
 };
 
+// The state entering every kBwdBlock-step block: [batch][ceil(L / kBwdBlock)][N][dim] fp32.
+size_t checkpoint_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t N) {
+  const int64_t nblk = (seqlen + sscan::kBwdBlock - 1) / sscan::kBwdBlock;
+  return static_cast<size_t>(batch) * nblk * N * dim * sizeof(float);
+}
+
 size_t seg_workspace_bytes(int64_t batch, int64_t dim, int64_t N, int nseg) {
   if (nseg <= 1) return 0;
   // carry [nseg][B][D][N], end states [nseg][B][D][N], sums [nseg][B][D]
@@ -174,7 +180,8 @@ int check_conv(const ConvArgs& cv, int64_t batch, int64_t dim) {
 int fwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype, unsigned flags, const void* x,
              const void* delta, const float* A, const void* B, const void* C, const float* D, const void* z,
              const float* delta_bias, const float* initial_state, void* y, float* last_state, void* workspace,
-             size_t workspace_bytes, int64_t num_segments, void* stream, const ConvArgs& cv) {
+             size_t workspace_bytes, int64_t num_segments, void* stream, const ConvArgs& cv,
+             float* ckpt_out = nullptr, size_t ckpt_bytes = 0) {
   int rc = check_common(batch, dim, dstate, dtype, flags);
   if (rc) return rc;
   rc = check_conv(cv, batch, dim);
@@ -231,6 +238,17 @@ int fwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dty
     if (initial_state && initial_state != last_state && overlaps(initial_state, st, last_state, st))
       return fail(SSCAN_ERR_INVALID_ARG, "initial_state and last_state partially overlap");
   }
+  const int64_t nblk = (seqlen + sscan::kBwdBlock - 1) / sscan::kBwdBlock;
+  if (ckpt_out) {
+    const size_t need = checkpoint_bytes(batch, seqlen, dim, N);
+    if (!aligned(ckpt_out, 4)) return fail(SSCAN_ERR_INVALID_ARG, "checkpoints not 4-byte aligned");
+    if (ckpt_bytes < need)
+      return fail(SSCAN_ERR_INVALID_ARG, "checkpoint buffer too small (%zu < %zu bytes)", ckpt_bytes, need);
+    const Buf others[] = {{x, tok}, {delta, tok}, {z, tok}, {y, tok}, {B, bc}, {C, bc}, {last_state, st},
+                          {initial_state, st}, {A, static_cast<size_t>(N) * dim * 4}, {workspace, workspace_bytes}};
+    for (const Buf& o : others)
+      if (overlaps(ckpt_out, need, o.p, o.n)) return fail(SSCAN_ERR_INVALID_ARG, "checkpoints overlap a tensor");
+  }
   if (cv.state_out) {
     const Buf others[] = {{x, tok}, {delta, tok}, {z, tok}, {y, tok}, {B, bc}, {C, bc}, {last_state, st},
                           {initial_state, st}, {cv.w, static_cast<size_t>(dim) * cv.dconv * 4}};
@@ -252,6 +270,7 @@ int fwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dty
   p.npw = fwd_states_per_wave(N, p.ndtiles * batch * pl.nseg);
   p.euler = (flags & SSCAN_FLAG_EULER) != 0;
   p.conv_w = cv.w; p.conv_b = cv.b; p.conv_s = cv.state_in; p.dconv = static_cast<int>(cv.w ? cv.dconv : 0);
+  p.ckpt = ckpt_out; p.nblk = nblk;
   const bool bf16 = dtype == SSCAN_BF16;
   // the convolution state leaves after the scan (which reads the incoming one)
   auto finish = [&]() -> int {
@@ -295,6 +314,7 @@ size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct BwdLayout {
   size_t ckpt, gB, gC, gA, gD, gb, seg, rg, rs, gin, total;
+  size_t total_saved;      // bytes needed when the checkpoints come from the caller
   int nseg;                // forward (checkpoint) pass segments
   int64_t seg_len;
   int bseg;                // reverse pass segments
@@ -322,7 +342,6 @@ BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t N) {
   if (lo.bseg < 1) lo.bseg = 1;
   const size_t bdn = static_cast<size_t>(batch) * dim * N;
   size_t off = 0;
-  lo.ckpt = off; off += round256(static_cast<size_t>(batch) * nblk * N * dim * 4);
   lo.gB = off;   off += round256(static_cast<size_t>(ndt) * batch * N * seqlen * 4);
   lo.gC = off;   off += round256(static_cast<size_t>(ndt) * batch * N * seqlen * 4);
   lo.gA = off;   off += round256(static_cast<size_t>(lo.bseg) * bdn * 4);
@@ -336,6 +355,9 @@ BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t N) {
   lo.rg = off;   off += round256(nb * bdn * 4);
   lo.rs = off;   off += round256(nb * batch * dim * 4);
   lo.gin = off;  off += round256(nb * bdn * 4);
+  lo.total_saved = off;
+  // the checkpoints come last, so a caller that supplies its own can pass less
+  lo.ckpt = off; off += round256(checkpoint_bytes(batch, seqlen, dim, N));
   lo.total = off;
   return lo;
 }
@@ -344,13 +366,16 @@ int bwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dty
              const void* delta, const float* A, const void* B, const void* C, const float* D, const void* z,
              const float* delta_bias, const float* initial_state, const void* dy, const float* dlast_state,
              void* dx, void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz, float* ddelta_bias,
-             float* dinitial_state, void* workspace, size_t workspace_bytes, void* stream) {
+             float* dinitial_state, void* workspace, size_t workspace_bytes, void* stream,
+             const float* ckpt_in = nullptr, size_t ckpt_bytes = 0, bool saved = false) {
   int rc = check_common(batch, dim, dstate, dtype, flags);
   if (rc) return rc;
   if (seqlen < 0) return fail(SSCAN_ERR_INVALID_ARG, "negative seqlen %lld", (long long)seqlen);
   const int64_t max_elems = (int64_t(1) << 62) / 8;
   if (batch > 0 && dim > 0 && seqlen > max_elems / batch / dim)
     return fail(SSCAN_ERR_INVALID_ARG, "batch*seqlen*dim too large");
+  if (saved && seqlen > 0 && batch > 0 && dim > 0 && !ckpt_in)
+    return fail(SSCAN_ERR_INVALID_ARG, "null required pointer (checkpoints)");
   if ((z == nullptr) != (dz == nullptr)) return fail(SSCAN_ERR_INVALID_ARG, "dz must be given exactly when z is");
   if (dD && !D) return fail(SSCAN_ERR_INVALID_ARG, "dD requested without D");
   if (dim > (int64_t(1) << 27)) return fail(SSCAN_ERR_INVALID_ARG, "dim too large for the backward pass");
@@ -380,8 +405,15 @@ int bwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dty
   if (!workspace || !aligned(workspace, 256))
     return fail(SSCAN_ERR_INVALID_ARG, "workspace missing or not 256-byte aligned");
   const BwdLayout lo = bwd_layout(batch, seqlen, dim, N);
-  if (workspace_bytes < lo.total)
-    return fail(SSCAN_ERR_INVALID_ARG, "workspace too small (%zu < %zu bytes)", workspace_bytes, lo.total);
+  const size_t ws_need = saved ? lo.total_saved : lo.total;
+  if (workspace_bytes < ws_need)
+    return fail(SSCAN_ERR_INVALID_ARG, "workspace too small (%zu < %zu bytes)", workspace_bytes, ws_need);
+  if (saved) {
+    const size_t need = checkpoint_bytes(batch, seqlen, dim, N);
+    if (!aligned(ckpt_in, 4)) return fail(SSCAN_ERR_INVALID_ARG, "checkpoints not 4-byte aligned");
+    if (ckpt_bytes < need)
+      return fail(SSCAN_ERR_INVALID_ARG, "checkpoint buffer too small (%zu < %zu bytes)", ckpt_bytes, need);
+  }
 
   const size_t tok = static_cast<size_t>(batch) * seqlen * dim * es;
   const size_t bc = static_cast<size_t>(batch) * seqlen * N * es;
@@ -389,9 +421,14 @@ int bwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dty
   const Buf inputs[] = {{x, tok}, {delta, tok}, {z, tok}, {dy, tok}, {B, bc}, {C, bc}, {A, size_t(dim) * N * 4},
                         {D, size_t(dim) * 4}, {delta_bias, size_t(dim) * 4}, {initial_state, st},
                         {dlast_state, st}};
+  const size_t ckn = saved ? checkpoint_bytes(batch, seqlen, dim, N) : 0;
+  const Buf inputs2[] = {{ckpt_in, ckn}};
   const Buf outputs[] = {{dx, tok}, {ddelta, tok}, {dz, tok}, {dB, bc}, {dC, bc}, {dA, size_t(dim) * N * 4},
                          {dD, size_t(dim) * 4}, {ddelta_bias, size_t(dim) * 4}, {dinitial_state, st},
-                         {workspace, lo.total}};
+                         {workspace, ws_need}};
+  for (const Buf& o : outputs)
+    for (const Buf& i : inputs2)
+      if (overlaps(o.p, o.n, i.p, i.n)) return fail(SSCAN_ERR_INVALID_ARG, "an output overlaps the checkpoints");
   for (const Buf& o : outputs) {
     for (const Buf& i : inputs)
       if (overlaps(o.p, o.n, i.p, i.n)) return fail(SSCAN_ERR_INVALID_ARG, "an output overlaps an input");
@@ -404,8 +441,9 @@ int bwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dty
   const bool euler = (flags & SSCAN_FLAG_EULER) != 0;
   const int64_t nblk = (seqlen + sscan::kBwdBlock - 1) / sscan::kBwdBlock;
   const int64_t ndt = (dim + sscan::kTile - 1) / sscan::kTile;
-  float* ckpt = reinterpret_cast<float*>(ws + lo.ckpt);
-
+  const float* ckpt = saved ? ckpt_in : reinterpret_cast<const float*>(ws + lo.ckpt);
+  hipError_t e;
+  if (!saved) {
   // 1. checkpoints: the forward recurrence, storing the state entering every chunk
   sscan::FwdParams p{};
   p.x = x; p.dt = delta; p.z = nullptr; p.B = B; p.C = C;
@@ -416,8 +454,7 @@ int bwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dty
   p.seg_len = lo.seg_len; p.nseg = lo.nseg;
   p.npw = 1;
   p.euler = euler;
-  p.ckpt = ckpt;
-  hipError_t e;
+  p.ckpt = reinterpret_cast<float*>(ws + lo.ckpt);
   if (lo.nseg == 1) {
     p.h_init = initial_state;
   } else {
@@ -435,6 +472,7 @@ int bwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dty
   }
   e = sscan::launch_fwd_checkpoints(p, bf16, s);
   if (e != hipSuccess) return hip_fail(e, "checkpoint launch");
+  }
 
   // 2. reverse pass and reductions
   sscan::BwdParams q{};
@@ -528,6 +566,22 @@ int sscan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dt
                   last_state, workspace, workspace_bytes, 0, stream, ConvArgs{});
 }
 
+size_t sscan_checkpoint_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
+  if (batch <= 0 || seqlen <= 0 || dim <= 0 || dstate < 1 || dstate > SSCAN_MAX_DSTATE) return 0;
+  return checkpoint_bytes(batch, seqlen, dim, dstate);
+}
+
+int sscan_fwd_checkpointed(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+                           unsigned int flags, const void* x, const void* delta, const float* A, const void* B,
+                           const void* C, const float* D, const void* z, const float* delta_bias,
+                           const float* initial_state, void* y, float* last_state, void* workspace,
+                           size_t workspace_bytes, float* checkpoints, size_t checkpoint_bytes_, void* stream) {
+  if (!checkpoints && batch > 0 && seqlen > 0 && dim > 0)
+    return fail(SSCAN_ERR_INVALID_ARG, "null required pointer (checkpoints)");
+  return fwd_impl(batch, seqlen, dim, dstate, dtype, flags, x, delta, A, B, C, D, z, delta_bias, initial_state, y,
+                  last_state, workspace, workspace_bytes, 0, stream, ConvArgs{}, checkpoints, checkpoint_bytes_);
+}
+
 int sscan_fwd_conv(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int64_t dconv, int dtype,
                    unsigned int flags, const void* x, const float* conv_w, const float* conv_b,
                    const float* conv_state_in, float* conv_state_out, const void* delta, const float* A,
@@ -580,6 +634,23 @@ int sscan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dt
   return bwd_impl(batch, seqlen, dim, dstate, dtype, flags, x, delta, A, B, C, D, z, delta_bias, initial_state, dy,
                   dlast_state, dx, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dinitial_state, workspace,
                   workspace_bytes, stream);
+}
+
+size_t sscan_bwd_checkpointed_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype) {
+  (void)dtype;
+  if (batch <= 0 || seqlen <= 0 || dim <= 0 || dstate < 1 || dstate > SSCAN_MAX_DSTATE) return 0;
+  return bwd_layout(batch, seqlen, dim, dstate).total_saved;
+}
+
+int sscan_bwd_checkpointed(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype, unsigned int flags,
+                           const void* x, const void* delta, const float* A, const void* B, const void* C,
+                           const float* D, const void* z, const float* delta_bias, const float* checkpoints,
+                           size_t checkpoint_bytes_, const void* dy, const float* dlast_state, void* dx,
+                           void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz, float* ddelta_bias,
+                           float* dinitial_state, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(batch, seqlen, dim, dstate, dtype, flags, x, delta, A, B, C, D, z, delta_bias, nullptr, dy,
+                  dlast_state, dx, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dinitial_state, workspace,
+                  workspace_bytes, stream, checkpoints, checkpoint_bytes_, true);
 }
 
 }  // extern "C"

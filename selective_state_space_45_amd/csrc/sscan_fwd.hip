@@ -11,6 +11,8 @@ extern template hipError_t launch_fwd_variant<kFwdCkpt, false, false>(const FwdP
 extern template hipError_t launch_fwd_variant<kFwdOut, true, false>(const FwdParams&, bool, hipStream_t);
 extern template hipError_t launch_fwd_variant<kFwdAgg, true, false>(const FwdParams&, bool, hipStream_t);
 extern template hipError_t launch_fwd_variant<kFwdCkpt, true, false>(const FwdParams&, bool, hipStream_t);
+extern template hipError_t launch_fwd_variant<kFwdOutCkpt, false, false>(const FwdParams&, bool, hipStream_t);
+extern template hipError_t launch_fwd_variant<kFwdOutCkpt, true, false>(const FwdParams&, bool, hipStream_t);
 extern template hipError_t launch_fwd_variant<kFwdOut, false, true>(const FwdParams&, bool, hipStream_t);
 extern template hipError_t launch_fwd_variant<kFwdAgg, false, true>(const FwdParams&, bool, hipStream_t);
 extern template hipError_t launch_fwd_variant<kFwdOut, true, true>(const FwdParams&, bool, hipStream_t);
@@ -58,7 +60,7 @@ namespace {
 
 template <int MODE>
 hipError_t launch_fwd_mode(const FwdParams& p, bool bf16, hipStream_t s) {
-  if constexpr (MODE != kFwdCkpt) {
+  if constexpr (MODE == kFwdOut || MODE == kFwdAgg) {   // the modes with a convolution prologue
     if (p.conv_w)
       return p.euler ? launch_fwd_variant<MODE, true, true>(p, bf16, s)
                      : launch_fwd_variant<MODE, false, true>(p, bf16, s);
@@ -96,6 +98,9 @@ __global__ __launch_bounds__(256) void conv_state_kernel(const Tin* __restrict__
 }  // namespace
 
 hipError_t launch_fwd_main(const FwdParams& p, bool bf16, hipStream_t s) {
+  // with a checkpoint array (and no convolution prologue) the output pass saves the
+  // backward pass's checkpoints as it goes
+  if (p.ckpt && !p.conv_w) return launch_fwd_mode<kFwdOutCkpt>(p, bf16, s);
   return launch_fwd_mode<kFwdOut>(p, bf16, s);
 }
 

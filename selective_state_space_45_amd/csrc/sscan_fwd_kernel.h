@@ -126,7 +126,8 @@ __device__ __forceinline__ int64_t after(int64_t v, float dep) {
 // One workgroup: (batch row b, 64-channel tile, segment); NSPLIT waves x NPW states.
 // MODE: kFwdOut (y and the final state), kFwdAgg (segment aggregates only: end state
 // from a zero start and sum of Delta), kFwdCkpt (no y: the state entering every
-// block of kBwdBlock steps is written to ckpt, for the backward pass).
+// block of kBwdBlock steps is written to ckpt, for the backward pass), kFwdOutCkpt
+// (both kFwdOut's and kFwdCkpt's outputs).
 // NFIX: N as a compile-time constant (0 = read it from the shape at run time).
 // EULER: Bbar = Delta B instead of the zero-order hold.
 // CONV: x is the raw input of a causal depthwise convolution over time (sh.dconv
@@ -143,8 +144,8 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
     float* __restrict__ ckpt, const float* __restrict__ conv_w, const float* __restrict__ conv_b,
     const float* __restrict__ conv_s, FwdShape sh) {
   constexpr bool AGG = MODE == kFwdAgg;
-  constexpr bool OUT = MODE == kFwdOut;
-  constexpr bool CKPT = MODE == kFwdCkpt;
+  constexpr bool OUT = MODE == kFwdOut || MODE == kFwdOutCkpt;
+  constexpr bool CKPT = MODE == kFwdCkpt || MODE == kFwdOutCkpt;
   constexpr int T = kChunk;
   constexpr int TPW = T / NSPLIT;  // prologue/epilogue timesteps per wave per chunk
   constexpr int H = T / 2;

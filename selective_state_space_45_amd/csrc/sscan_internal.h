@@ -15,6 +15,7 @@ constexpr int kMaxConv = 4;   // taps of the fused convolution prologue (Mamba's
 constexpr int kFwdOut = 0;    // y (and the final state)
 constexpr int kFwdAgg = 1;    // per-segment aggregates for the two-level scan
 constexpr int kFwdCkpt = 2;   // states entering every kBwdBlock steps, for the backward pass
+constexpr int kFwdOutCkpt = 3;  // y and the final state, and the kFwdCkpt states as well
 
 struct FwdParams {
   const void* x;

@@ -29,6 +29,13 @@ def lib():
     lb.sscan_bwd.argtypes = [I64, I64, I64, I64, ctypes.c_int, U32] + [P] * 21 + [SZ, P]
     lb.sscan_fwd_conv.argtypes = [I64, I64, I64, I64, I64, ctypes.c_int, U32] + [P] * 15 + [P, SZ, P]
     lb.sscan_step_conv.argtypes = [I64, I64, I64, I64, ctypes.c_int, U32] + [P] * 14
+    lb.sscan_checkpoint_bytes.argtypes = [I64, I64, I64, I64]
+    lb.sscan_checkpoint_bytes.restype = SZ
+    lb.sscan_fwd_checkpointed.argtypes = [I64, I64, I64, I64, ctypes.c_int, U32] + [P] * 11 + [P, SZ, P, SZ, P]
+    lb.sscan_bwd_checkpointed_workspace_size.argtypes = [I64, I64, I64, I64, ctypes.c_int]
+    lb.sscan_bwd_checkpointed_workspace_size.restype = SZ
+    lb.sscan_bwd_checkpointed.argtypes = ([I64, I64, I64, I64, ctypes.c_int, U32] + [P] * 8 + [P, SZ] + [P] * 11
+                                          + [P, SZ, P])
     return lb
 
 
@@ -42,7 +49,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for must in ("sscan_fwd", "sscan_step", "sscan_fwd_segmented", "sscan_fwd_workspace_size",
                  "sscan_bwd", "sscan_bwd_workspace_size", "sscan_fwd_conv", "sscan_step_conv",
-                 "sscan_last_error", "sscan_version"):
+                 "sscan_checkpoint_bytes", "sscan_fwd_checkpointed", "sscan_bwd_checkpointed",
+                 "sscan_bwd_checkpointed_workspace_size", "sscan_last_error", "sscan_version"):
         assert must in names
 
 
@@ -200,3 +208,49 @@ def test_conv_validation(lib):
     assert lib.sscan_step_conv(4, 8, 4, 4, 0, 0, *args) == 1
     assert b"conv_state" in lib.sscan_last_error()
     assert lib.sscan_step_conv(4, 8, 4, 9, 0, 0, *args) == 2
+
+
+def test_checkpoint_sizes(lib):
+    # the state entering every 8 steps: [batch][ceil(L/8)][N][dim] float32
+    assert lib.sscan_checkpoint_bytes(8, 4096, 2048, 16) == 8 * 512 * 16 * 2048 * 4
+    assert lib.sscan_checkpoint_bytes(2, 53, 100, 5) == 2 * 7 * 5 * 100 * 4
+    assert lib.sscan_checkpoint_bytes(2, 0, 100, 5) == 0
+    full = lib.sscan_bwd_workspace_size(8, 4096, 2048, 16, 1)
+    saved = lib.sscan_bwd_checkpointed_workspace_size(8, 4096, 2048, 16, 1)
+    assert full - saved == 8 * 512 * 16 * 2048 * 4
+
+
+def fwd_ck(lib, ck=FAKE, ckb=1 << 20, batch=2, L=8, dim=4, N=4):
+    P = ctypes.c_void_p
+    return lib.sscan_fwd_checkpointed(batch, L, dim, N, 0, 0, FAKE, FAKE2, P(0x30000), P(0x40000), P(0x50000), None,
+                                      None, None, None, P(0x60000), None, None, 0, ck, ckb, None)
+
+
+def test_fwd_checkpointed_validation(lib):
+    assert fwd_ck(lib, ck=None) == 1
+    assert b"checkpoints" in lib.sscan_last_error()
+    assert fwd_ck(lib, ckb=2 * 1 * 4 * 4 * 4 - 4) == 1            # one block short of 4 bytes
+    assert b"too small" in lib.sscan_last_error()
+    assert fwd_ck(lib, ck=ctypes.c_void_p(0x10002)) == 1           # misaligned
+    assert fwd_ck(lib, ck=ctypes.c_void_p(0x60000)) == 1           # overlaps y
+    assert b"overlap" in lib.sscan_last_error()
+    assert fwd_ck(lib, N=17) == 2
+
+
+def bwd_ck(lib, ck=ctypes.c_void_p(0x70000), ckb=1 << 20, wsb=1 << 20, N=4):
+    P = ctypes.c_void_p
+    return lib.sscan_bwd_checkpointed(2, 8, 4, N, 0, 0, FAKE, FAKE2, P(0x30000), P(0x40000), P(0x50000), None,
+                                      None, None, ck, ckb, P(0x60000), None, P(0x80000), P(0x90000), P(0xa0000),
+                                      P(0xb0000), P(0xc0000), None, None, None, None, P(0x100000), wsb, None)
+
+
+def test_bwd_checkpointed_validation(lib):
+    assert bwd_ck(lib, ck=None) == 1
+    assert b"checkpoints" in lib.sscan_last_error()
+    assert bwd_ck(lib, ckb=8) == 1
+    assert b"too small" in lib.sscan_last_error()
+    assert bwd_ck(lib, wsb=16) == 1
+    assert b"workspace" in lib.sscan_last_error()
+    assert bwd_ck(lib, ck=ctypes.c_void_p(0x80000)) == 1            # the checkpoints are dx
+    assert b"overlap" in lib.sscan_last_error()
+    assert bwd_ck(lib, N=17) == 2
