@@ -113,3 +113,14 @@ def test_bwd_checkpointed_no_dlast_no_gate(ss, orc):
     w = W.make_scan_inputs(1, 70, 64, 16, "bf16", seed=940, with_z=False, with_D=False, with_bias=False,
                            name="bwd ck minimal")
     check_bwd_ck(ss, orc, w, with_dlast=False)
+
+
+@pytest.mark.timeout(600)
+def test_bwd_checkpointed_mamba130m_layer(ss, orc):
+    # 48 workgroups: split sequence in both directions
+    check_bwd_ck(ss, orc, W.workload("mamba130m_layer"))
+
+
+@pytest.mark.timeout(900)
+def test_bwd_checkpointed_train_shape(ss, orc):
+    check_bwd_ck(ss, orc, W.workload("train_shape"))
