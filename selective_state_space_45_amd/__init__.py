@@ -167,6 +167,8 @@ def sscan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Te
     if conv_w is not None:
         if num_segments is not None:
             raise ValueError("num_segments is not available with the convolution prologue")
+        if checkpoints is not None:
+            raise ValueError("checkpoints are not available with the convolution prologue")
         dconv = conv_w.shape[1] if conv_w.dim() == 2 else -1
         _dev(conv_w, "conv_w", torch.float32, (dim, dconv))
         if conv_b is not None:

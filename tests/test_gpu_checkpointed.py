@@ -124,3 +124,16 @@ def test_bwd_checkpointed_mamba130m_layer(ss, orc):
 @pytest.mark.timeout(900)
 def test_bwd_checkpointed_train_shape(ss, orc):
     check_bwd_ck(ss, orc, W.workload("train_shape"))
+
+
+def test_checkpoints_rejected_with_conv_or_segments(ss):
+    import torch
+    w = W.make_scan_inputs(1, 16, 64, 4, "f32", seed=950, name="ck validation")
+    args = (tdev(w.x, "f32"), tdev(w.dt, "f32"), f32dev(w.A), tdev(w.B, "f32"), tdev(w.C, "f32"))
+    ck = torch.empty(ss.checkpoint_bytes(1, 16, 64, 4) // 4, dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError, match="checkpoints"):
+        ss.sscan_fwd(*args, conv_w=torch.ones(64, 4, device="cuda"), checkpoints=ck)
+    with pytest.raises(ValueError, match="checkpoints"):
+        ss.sscan_fwd(*args, num_segments=2, checkpoints=ck)
+    with pytest.raises(ss.SelScanError):     # one float short of the checkpoint array
+        ss.sscan_fwd(*args, checkpoints=ck[1:])
