@@ -171,14 +171,34 @@ def per_config_report() -> None:
         err = float(np.max(np.abs(yg - yr) / (1.0 + np.abs(yr))))
         es = float(np.max(np.abs(st.cpu().numpy() - sr) / (1.0 + np.abs(sr))))
         tokch = w.batch * w.seqlen * w.dim
+        # backward pass on the same workload (errors are checked by the parity tests):
+        # sscan_bwd alone, and a training step's forward-with-checkpoints + backward
+        gy = torch.randn_like(x)
+        bws = torch.empty(ss.bwd_workspace_size(w.batch, w.seqlen, w.dim, w.dstate, x.dtype), dtype=torch.uint8,
+                          device=dev)
+        grads = {}
+        bwd_ms = median_ms(lambda: ss.sscan_bwd(x, dt, A, B, C, gy, D=D, z=z, delta_bias=bias, workspace=bws,
+                                                out=grads), n=5, warm=2)
+        ck = torch.empty(ss.checkpoint_bytes(w.batch, w.seqlen, w.dim, w.dstate) // 4, dtype=torch.float32,
+                         device=dev)
+        fck_ms = median_ms(lambda: ss.sscan_fwd(x, dt, A, B, C, D=D, z=z, delta_bias=bias, out=y, last_state=st,
+                                                workspace=ws, checkpoints=ck), n=5, warm=2)
+        bck_ms = median_ms(lambda: ss.sscan_bwd(x, dt, A, B, C, gy, D=D, z=z, delta_bias=bias, workspace=bws,
+                                                out=grads, checkpoints=ck), n=5, warm=2)
         print(json.dumps({"config": name, "shape": [w.batch, w.seqlen, w.dim, w.dstate], "dtype": w.dtype,
                           "gpu_ms_median": round(ms, 5), "tokens_channels_per_s": round(tokch / (ms * 1e-3), 1),
                           "gbs": round(nb / (ms * 1e-3) / 1e9, 2), "hbm_frac": round(nb / (ms * 1e-3) / 1e9 / 8000, 4),
                           "segments": "auto" if wsb else 1, "max_err_y": err, "max_err_state": es,
                           "tol": 1e-4 if w.dtype == "f32" else 2e-2, "oracle_s": round(cpu_s, 3),
                           "oracle_threads": oracle.last_threads_used(),
-                          "oracle_tokens_channels_per_s": round(tokch / cpu_s, 1)}), flush=True)
-        del x, dt, z, B, C, y, st, ws
+                          "oracle_tokens_channels_per_s": round(tokch / cpu_s, 1),
+                          "bwd_ms_median": round(bwd_ms, 5),
+                          "train_step_ms_median": {"fwd_checkpointed": round(fck_ms, 5),
+                                                   "bwd_checkpointed": round(bck_ms, 5),
+                                                   "total": round(fck_ms + bck_ms, 5),
+                                                   "vs_fwd_plus_bwd": round(ms + bwd_ms, 5)}}), flush=True)
+        del x, dt, z, B, C, y, st, ws, gy, bws, grads, ck
+        torch.cuda.empty_cache()
 
     dw = W.DecodeWorkload()
     tk = dw.token(0)
