@@ -37,7 +37,8 @@ OPS_PER_TOKEN_CHANNEL = 20   # softplus 11, silu 7, skip + gate 2
 PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "sscan_fwd_train_shape_counters.json")
 COPY_ELEMS = 128 << 20                       # calibration copy: 512 MiB of fp32
 KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_45_amd", "csrc", f)
-                  for f in ("sscan_fwd_kernel.h", "sscan_fwd_zoh.hip", "sscan_device.h", "sscan_internal.h")]
+                  for f in ("sscan_fwd_row.h", "sscan_fwd_row_zoh.hip", "sscan_fwd_kernel.h", "sscan_device.h",
+                            "sscan_internal.h")]
 
 
 def kernel_source_hash() -> str:
@@ -91,13 +92,13 @@ def summarize_counters(fetch_csv: str, write_csv: str) -> dict:
     # the 512 MiB copy: 2^27 floats, four per thread
     calib = " grid=%d" % (COPY_ELEMS // 4)
     pick = lambda tab: next(v for k, v in tab.items() if "AUnaryFunctor" in k and k.endswith(calib))
-    # the forward kernel in its output mode (4th template argument 0) with the
-    # zero-order hold and no convolution prologue (last two arguments false)
+    # the forward kernel in its output mode (2nd template argument 0) with the
+    # zero-order hold (last argument false)
     def zoh(k):
-        if "sscan::fwd_kernel<" not in k:
+        if "sscan::fwd_row_kernel<" not in k:
             return False
         args = [a.strip() for a in k.split("(")[0].split("<", 1)[1].rstrip(">").split(",")]
-        return args[3] == "0" and args[-2:] == ["false", "false"]
+        return args[1] == "0" and args[-1] == "false"
     copy_bytes = COPY_ELEMS * 4
     ff = copy_bytes / (pick(fetch) * 1024)
     fw = copy_bytes / (pick(write) * 1024)
@@ -475,7 +476,7 @@ def main():
         "roofline": {"bound": "alu", "achieved": round(achieved_tops, 3), "peak": round(PEAK_VALU_TOPS, 3),
                      "unit": "Top/s", "frac": round(achieved_tops / PEAK_VALU_TOPS, 4),
                      "traffic": measured_traffic(),
-                     "kernel": "fwd_kernel<bf16, 16 waves x 1 state, main, paired B/C, N=16>",
+                     "kernel": "fwd_row_kernel<bf16, output mode, N=16, zero-order hold>",
                      "kernel_ms": round(kern_ms, 5), "kernel_gbs": round(kern_gbs, 2),
                      "algorithmic_bytes": nbytes, "algorithmic_ops": ops},
         "euler": euler,

@@ -121,6 +121,8 @@ hipError_t launch_bwd(const BwdParams& p, bool bf16, hipStream_t s);
 
 // Waves per workgroup of the forward kernel with npw states per wave.
 int fwd_nsplit(int npw, int N);
+// Whether a forward launch takes the row layout (fwd_row_kernel).
+bool fwd_row_layout(const FwdParams& p);
 
 // Launchers; return hipSuccess or the launch error.
 hipError_t launch_fwd_main(const FwdParams& p, bool bf16, hipStream_t s);
