@@ -45,13 +45,6 @@ namespace sscan {
 
 namespace {
 
-__device__ __forceinline__ int64_t bwd_xcd_remap(int64_t bid, int64_t nblk) {
-  constexpr int64_t kXcd = 8;
-  const int64_t per = nblk / kXcd, rem = nblk % kXcd;
-  const int64_t xcd = bid % kXcd, slot = bid / kXcd;
-  return (xcd < rem) ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
-}
-
 // Value of v in the lane that DPP control CTRL selects (a permutation within rows).
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
@@ -188,7 +181,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tid = threadIdx.x;
 
-  int64_t blk = bwd_xcd_remap(blockIdx.x, sh.ndtiles * sh.batch * sh.nseg);
+  int64_t blk = xcd_remap(blockIdx.x, sh.ndtiles * sh.batch * sh.nseg);
   const int64_t dtile = blk % sh.ndtiles;
   blk /= sh.ndtiles;
   const int64_t b = blk % sh.batch;
@@ -535,7 +528,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_agg_kernel(
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tid = threadIdx.x;
   // segments 1 .. nseg-1 (the first segment's aggregate is never needed)
-  int64_t blk = bwd_xcd_remap(blockIdx.x, sh.ndtiles * sh.batch * (sh.nseg - 1));
+  int64_t blk = xcd_remap(blockIdx.x, sh.ndtiles * sh.batch * (sh.nseg - 1));
   const int64_t dtile = blk % sh.ndtiles;
   blk /= sh.ndtiles;
   const int64_t b = blk % sh.batch;

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace sscan {
 
 typedef uint16_t bf16_t;  // bfloat16 storage word
@@ -37,5 +39,20 @@ __device__ __forceinline__ float softplus_log2e(float v2) {
 
 // silu(z) = z * sigmoid(z) = z / (1 + e^{-z}).
 __device__ __forceinline__ float silu(float z) { return z * hw_rcp(1.f + hw_exp2(-z * kLog2e)); }
+
+// Compile-time LDS buffer index (double-buffered pipelines).
+template <int P>
+using Par = std::integral_constant<int, P>;
+
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2).
+// Remap the dispatch index so that consecutive logical blocks -- neighbouring
+// channel tiles of one batch row, which read the same B and C rows -- run on
+// the same XCD.  The map is a bijection of [0, nblk).
+__device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t nblk) {
+  constexpr int64_t kXcd = 8;
+  const int64_t per = nblk / kXcd, rem = nblk % kXcd;
+  const int64_t xcd = bid % kXcd, slot = bid / kXcd;
+  return (xcd < rem) ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+}
 
 }  // namespace sscan

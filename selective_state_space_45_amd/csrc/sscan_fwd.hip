@@ -9,10 +9,8 @@ namespace sscan {
 
 extern template hipError_t launch_fwd_variant<kFwdOut, false, false>(const FwdParams&, bool, hipStream_t);
 extern template hipError_t launch_fwd_variant<kFwdAgg, false, false>(const FwdParams&, bool, hipStream_t);
-extern template hipError_t launch_fwd_variant<kFwdCkpt, false, false>(const FwdParams&, bool, hipStream_t);
 extern template hipError_t launch_fwd_variant<kFwdOut, true, false>(const FwdParams&, bool, hipStream_t);
 extern template hipError_t launch_fwd_variant<kFwdAgg, true, false>(const FwdParams&, bool, hipStream_t);
-extern template hipError_t launch_fwd_variant<kFwdCkpt, true, false>(const FwdParams&, bool, hipStream_t);
 extern template hipError_t launch_fwd_variant<kFwdOutCkpt, false, false>(const FwdParams&, bool, hipStream_t);
 extern template hipError_t launch_fwd_variant<kFwdOutCkpt, true, false>(const FwdParams&, bool, hipStream_t);
 extern template hipError_t launch_fwd_variant<kFwdOut, false, true>(const FwdParams&, bool, hipStream_t);
@@ -80,10 +78,13 @@ hipError_t launch_fwd_mode(const FwdParams& p, bool bf16, hipStream_t s) {
                      : launch_fwd_variant<MODE, false, true>(p, bf16, s);
   }
   if constexpr (MODE != kFwdAgg) {
-    if (fwd_row_layout(p))
+    // the checkpoint pass always runs one state per wave, hence the row layout
+    if (MODE == kFwdCkpt || fwd_row_layout(p))
       return p.euler ? launch_fwd_row<MODE, true>(p, bf16, s) : launch_fwd_row<MODE, false>(p, bf16, s);
   }
-  return p.euler ? launch_fwd_variant<MODE, true, false>(p, bf16, s) : launch_fwd_variant<MODE, false, false>(p, bf16, s);
+  if constexpr (MODE != kFwdCkpt)
+    return p.euler ? launch_fwd_variant<MODE, true, false>(p, bf16, s) : launch_fwd_variant<MODE, false, false>(p, bf16, s);
+  return hipErrorInvalidValue;
 }
 
 // out[b][d][k] = raw input at position L - (dconv-1) + k (from x, or from the incoming

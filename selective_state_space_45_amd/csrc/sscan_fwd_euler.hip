@@ -5,7 +5,6 @@ namespace sscan {
 
 template hipError_t launch_fwd_variant<kFwdOut, true, false>(const FwdParams&, bool, hipStream_t);
 template hipError_t launch_fwd_variant<kFwdAgg, true, false>(const FwdParams&, bool, hipStream_t);
-template hipError_t launch_fwd_variant<kFwdCkpt, true, false>(const FwdParams&, bool, hipStream_t);
 template hipError_t launch_fwd_variant<kFwdOutCkpt, true, false>(const FwdParams&, bool, hipStream_t);
 
 }  // namespace sscan

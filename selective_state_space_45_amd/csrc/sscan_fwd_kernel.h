@@ -42,9 +42,6 @@
 
 namespace sscan {
 
-template <int P>
-using Par = std::integral_constant<int, P>;
-
 // B values of a wave's NPW states at one timestep, kept as raw scalar words.
 // PAIR: bf16 with even N and 4-byte aligned B and C, so the wave's states sit in one
 // aligned dword (NPW = 2: both halves; NPW = 1: the half `sel` picks).  Otherwise NPW
@@ -96,17 +93,6 @@ __device__ __forceinline__ void load_c_row(const Tin* __restrict__ row, int N, f
   }
 }
 
-// Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2).
-// Remap the dispatch index so that consecutive logical blocks -- neighbouring
-// channel tiles of one batch row, which read the same B and C rows -- run on
-// the same XCD.  The map is a bijection of [0, nblk).
-__device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t nblk) {
-  constexpr int64_t kXcd = 8;
-  const int64_t per = nblk / kXcd, rem = nblk % kXcd;
-  const int64_t xcd = bid % kXcd, slot = bid / kXcd;
-  return (xcd < rem) ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
-}
-
 // Register-only barriers for the optimizer (no memory effects, no instructions).
 // opaque() hides how a scalar offset was computed, so per-timestep addresses are
 // formed as constant offsets from one base instead of separate induction variables;
@@ -127,7 +113,9 @@ __device__ __forceinline__ int64_t after(int64_t v, float dep) {
 // MODE: kFwdOut (y and the final state), kFwdAgg (segment aggregates only: end state
 // from a zero start and sum of Delta), kFwdCkpt (no y: the state entering every
 // block of kBwdBlock steps is written to ckpt, for the backward pass), kFwdOutCkpt
-// (both kFwdOut's and kFwdCkpt's outputs).
+// (both kFwdOut's and kFwdCkpt's outputs).  Launched are: the two-states-per-wave
+// main pass of split grids (kFwdOut, kFwdOutCkpt), the aggregate pass, and the
+// convolution prologue; the other launches run fwd_row_kernel (sscan_fwd_row.h).
 // NFIX: N as a compile-time constant (0 = read it from the shape at run time).
 // EULER: Bbar = Delta B instead of the zero-order hold.
 // CONV: x is the raw input of a causal depthwise convolution over time (sh.dconv
@@ -594,17 +582,22 @@ void launch_by_n(const FwdParams& p, dim3 grid, hipStream_t s) {
     }
     return;
   }
-  switch (fwd_nsplit(1, p.N)) {
-    case 1: launch_one<Tin, 1, 1, MODE, PR, 0, EU, CV>(p, grid, s); break;
-    case 2: launch_one<Tin, 2, 1, MODE, PR, 0, EU, CV>(p, grid, s); break;
-    case 4: launch_one<Tin, 4, 1, MODE, PR, 0, EU, CV>(p, grid, s); break;
-    case 8: launch_one<Tin, 8, 1, MODE, PR, 0, EU, CV>(p, grid, s); break;
-    default:
-      if (p.N == 16)
-        launch_one<Tin, 16, 1, MODE, PR, 16, EU, CV>(p, grid, s);
-      else
-        launch_one<Tin, 16, 1, MODE, PR, 0, EU, CV>(p, grid, s);
-      break;
+  // One state per wave: only the aggregate pass and the convolution prologue still
+  // take it (other one-state launches run fwd_row_kernel; launch_fwd_variant rejects
+  // them here).
+  if constexpr (MODE == kFwdAgg || CV) {
+    switch (fwd_nsplit(1, p.N)) {
+      case 1: launch_one<Tin, 1, 1, MODE, PR, 0, EU, CV>(p, grid, s); break;
+      case 2: launch_one<Tin, 2, 1, MODE, PR, 0, EU, CV>(p, grid, s); break;
+      case 4: launch_one<Tin, 4, 1, MODE, PR, 0, EU, CV>(p, grid, s); break;
+      case 8: launch_one<Tin, 8, 1, MODE, PR, 0, EU, CV>(p, grid, s); break;
+      default:
+        if (p.N == 16)
+          launch_one<Tin, 16, 1, MODE, PR, 16, EU, CV>(p, grid, s);
+        else
+          launch_one<Tin, 16, 1, MODE, PR, 0, EU, CV>(p, grid, s);
+        break;
+    }
   }
 }
 
@@ -613,6 +606,8 @@ void launch_by_n(const FwdParams& p, dim3 grid, hipStream_t s) {
 // parallel.
 template <int MODE, bool EU, bool CV>
 hipError_t launch_fwd_variant(const FwdParams& p, bool bf16, hipStream_t s) {
+  static_assert(MODE != kFwdCkpt, "the checkpoint pass runs fwd_row_kernel");
+  if (!(MODE == kFwdAgg || CV) && !(p.npw == 2 && p.N >= 3)) return hipErrorInvalidValue;
   const int64_t nblocks = p.ndtiles * p.batch * (MODE == kFwdAgg ? (p.nseg - 1) : p.nseg);
   if (nblocks <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(nblocks));

@@ -40,7 +40,6 @@
 #pragma once
 
 #include "sscan_device.h"
-#include "sscan_fwd_kernel.h"
 #include "sscan_internal.h"
 
 namespace sscan {
