@@ -1,0 +1,88 @@
+"""Static checks on the gfx950 assembly of the row-layout forward kernel (CPU only:
+hipcc cross-compiles; nothing runs on a GPU).
+
+A DPP read takes its value from another lane.  If that lane is switched off in the
+exec mask at that instruction, the read returns zero (bound_ctrl) instead of the
+lane's value, with no error.  fwd_row_kernel broadcasts Delta across each 16-lane row
+with DPP (row_newbcast) and reduces C.h across the row with DPP adds, so every DPP
+instruction must execute with the whole row active.  An earlier version computed the
+A == 0 branch's Delta inside a per-lane select, which the compiler lowered to an
+exec-masked block: the zero-A backward test caught the wrong results on the GPU.
+This test pins the property on the compiled code instead.
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "selective_state_space_45_amd", "csrc")
+
+
+def _hipcc():
+    cand = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
+    return cand if os.path.exists(cand) else shutil.which("hipcc")
+
+
+def _compile_asm(src, out):
+    from selective_state_space_45_amd.build import HIPCC_FLAGS
+    flags = [f for f in HIPCC_FLAGS if f not in ("-shared", "-fPIC")]
+    cmd = [_hipcc()] + flags + ["-I" + os.path.join(ROOT, "include"), "--cuda-device-only", "-S", "-o", out,
+                                os.path.join(CSRC, src)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    with open(out) as f:
+        return f.read()
+
+
+def dpp_under_partial_exec(asm: str, name_pattern: str):
+    """{kernel: (dpp instructions, dpp instructions inside an exec-masked block)}.
+
+    An exec-masked block opens at an s_and_saveexec_b64 (or s_andn2_saveexec_b64) and
+    closes at the matching `s_or_b64 exec, exec, ...` restore; the compiler emits
+    structured control flow in this form."""
+    out = {}
+    for name in re.findall(r"^(%s):" % name_pattern, asm, re.M):
+        start = asm.index(name + ":")
+        end = asm.index(".Lfunc_end", start)
+        depth = total = masked = 0
+        for line in asm[start:end].split("\n"):
+            t = line.strip()
+            if not t or t.startswith((";", ".")):
+                continue
+            op = t.split()[0]
+            if op.startswith(("s_and_saveexec", "s_andn2_saveexec")):
+                depth += 1
+            elif t.startswith("s_or_b64 exec, exec"):
+                depth = max(0, depth - 1)
+            if op.endswith("_dpp"):
+                total += 1
+                masked += depth > 0
+        out[name] = (total, masked)
+    return out
+
+
+def test_checker_flags_a_masked_dpp():
+    # the checker itself, on a hand-written fragment: one DPP move inside a
+    # saveexec/restore pair, one outside
+    asm = "\n".join(["_ZN5sscan14fwd_row_kernelItLi0E:",
+                     "  v_mov_b32_dpp v1, v2 row_newbcast:3 row_mask:0xf bank_mask:0xf",
+                     "  s_and_saveexec_b64 s[4:5], vcc",
+                     "  v_mul_f32_dpp v3, v2, v4 row_newbcast:1 row_mask:0xf bank_mask:0xf",
+                     "  s_or_b64 exec, exec, s[4:5]",
+                     ".Lfunc_end0:"])
+    res = dpp_under_partial_exec(asm, r"_ZN5sscan14fwd_row_kernel\w+")
+    assert list(res.values()) == [(2, 1)]
+
+
+@pytest.mark.skipif(_hipcc() is None, reason="hipcc not found")
+def test_row_kernel_dpp_runs_with_full_rows(tmp_path):
+    asm = _compile_asm("sscan_fwd_row_zoh.hip", str(tmp_path / "row_zoh.s"))
+    res = dpp_under_partial_exec(asm, r"_ZN5sscan14fwd_row_kernel\w+")
+    # output, checkpoint and output+checkpoint modes, bf16 and fp32, N = 16 and any N
+    assert len(res) == 12, sorted(res)
+    for name, (total, masked) in res.items():
+        assert total >= 16, (name, total)     # at least the 16 row broadcasts of a chunk
+        assert masked == 0, "%s: %d DPP instructions inside an exec-masked block" % (name, masked)
