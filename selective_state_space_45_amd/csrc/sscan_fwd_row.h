@@ -14,15 +14,12 @@
 //   prologue   wave w loads timestep w of the next chunk: x, dt, z coalesced along
 //              channels (lane = channel), softplus and silu once per (l, d), and two
 //              rows of B (waves 0-7) or C (waves 8-15); all of it staged to LDS.
-//   recurrence Delta*log2(e) of the chunk's timestep t for this lane's channel is
-//              read once per chunk (lane n of a row reads timestep n) and handed to
-//              every lane of the row by the DPP row broadcast (row_newbcast:t) inside
-//              the multiply by A, so the 16 steps need no further LDS reads for it.
-//              The products x_t B_t[n] of 4 timesteps come from one 16x16x4 f32 MFMA:
-//              its A operand holds x of (timestep, channel) on a diagonal, its B
-//              operand B[timestep][state], and its 16x16 result lands exactly in the
-//              (state, channel) lanes, one timestep per result register.  C of the
-//              lane's state for all 16 timesteps comes from LDS as four 128-bit reads.
+//   recurrence (Delta*log2(e), x) of the chunk's timestep t for this lane's channel is
+//              read once per chunk (lane n of a row reads timestep n, one 64-bit read)
+//              and handed to every lane of the row by the DPP row broadcast
+//              (row_newbcast:t) folded into the multiplies by A and by B, so the 16
+//              steps need no further LDS reads for them.  B and C of the lane's state
+//              for all 16 timesteps come from LDS as 128-bit reads (four each).
 //   readout    each lane forms C_t h_t for its state; the sum over the 16 states of a
 //              row is a reduce-scatter across the row's lanes (bank-masked DPP adds,
 //              then quad permutes) that leaves lane t of the row holding y's C.h for
@@ -32,9 +29,8 @@
 //              previous chunk, coalesced along channels.
 // Against fwd_kernel (one state per wave, lane = channel) this trades the per-step
 // LDS traffic -- every wave reading every staged (Delta, x) and the N-way readout of
-// states through LDS -- for DPP broadcasts, one small MFMA per 4 timesteps and a
-// register-only reduction; per wave and chunk the LDS traffic drops from ~16 KB to
-// ~5 KB.
+// states through LDS -- for DPP broadcasts and a register-only reduction; per wave and
+// chunk the LDS traffic drops from ~16 KB to ~9 KB, most of it 128-bit reads of B and C.
 // The state update is the same k-form: h <- Abar (h + k) - k with k = x B / A; a wave
 // whose channels have some A == 0 takes the explicit form, as a wave-uniform branch.
 #pragma once
@@ -156,19 +152,16 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
   static_assert(T == 16, "one staged timestep per lane of a row");
   static_assert(!CKPT || 2 * kBwdBlock == T, "checkpoints are taken at half chunks");
   // LDS layouts.  Row strides are chosen so that each read below touches distinct
-  // banks (32 lanes for 32-bit accesses, 8 lanes for 128-bit ones).
-  // Delta*log2(e) [timestep][channel]: the recurrence reads timestep = lane's state
-  // index, two rows per 32 lanes, hence a stride of 2 mod 32 words.
-  constexpr int DP = kTile + 2;
-  // x (Delta*x for the Euler rule) as the MFMA's A operand: row = channel, word
-  // 4*(t & 3) + (t >> 2) for timestep t; row kTile stays zero (off-diagonal lanes).
-  constexpr int XR = T + 4;
-  // B as the MFMA's B operand: row = state, same word order as x.
-  // C for the readout: row = state, word = timestep.
+  // banks (16 lanes for 64-bit accesses, 32 for 32-bit ones, 8 for 128-bit ones).
+  // (Delta*log2(e), x) [timestep][channel] (Delta*x for the Euler rule): the
+  // recurrence reads timestep = lane's state index, hence a row stride of 130 words,
+  // 2 mod 32.
+  constexpr int DP = kTile + 1;
+  // B and C: row = state, word = timestep; rows of 20 words keep 16-byte alignment
+  // and spread 8 consecutive rows over all 32 banks.
   constexpr int BR = T + 4;
   constexpr int YP = kTile + 2;
-  __shared__ float s_d[2][T][DP];
-  __shared__ __align__(16) float s_xt[2][kTile + 1][XR];
+  __shared__ float2 s_dx[2][T][DP];
   __shared__ __align__(16) float s_b[2][16][BR];
   __shared__ __align__(16) float s_c[OUT ? 2 : 1][16][BR];
   __shared__ float s_y[OUT ? 2 : 1][T][YP];
@@ -229,9 +222,6 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
   const float Av = nlive ? Ag[drc * N + ln] : -1.f;
   const float rA = (Av != 0.f) ? 1.f / Av : 0.f;
   const bool zeroA = __any(Av == 0.f);
-  // row of the x staging this lane feeds to the MFMA: its channel on the diagonal
-  // (lane bits 0-1 equal to its row), the zero row elsewhere
-  const int xrow = ((ln & 3) == lr) ? 4 * w + (ln >> 2) : kTile;
 
   float h = 0.f;
   if (h_init && drvalid && nlive) h = h_init[((static_cast<int64_t>(seg) * sh.batch + b) * dim + dr) * N + ln];
@@ -268,12 +258,11 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
       d2 = lv ? d2 : 0.f;
       xv = lv ? xv : 0.f;
     }
-    s_d[P][w][lane] = d2;
-    s_xt[P][lane][4 * (w & 3) + (w >> 2)] = EULER ? (d2 * kLn2) * xv : xv;
+    s_dx[P][w][lane] = make_float2(d2, EULER ? (d2 * kLn2) * xv : xv);
     if (bcwave && bclane) {
       const int t = bcrow0 + bcj;
       if (w < 8)
-        s_b[P][bcn][4 * (t & 3) + (t >> 2)] = to_f32(rbc);
+        s_b[P][bcn][t] = to_f32(rbc);
       else if constexpr (OUT)
         s_c[P][bcn][t] = to_f32(rbc);
     }
@@ -319,15 +308,13 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
     constexpr int P = decltype(pc)::value;
     constexpr int Q = 1 - P;
     constexpr bool STEADY = decltype(steadyc)::value;
-    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-    const float sd = s_d[P][ln][cr];
-    const f32x4 xa = *reinterpret_cast<const f32x4*>(&s_xt[P][xrow][4 * lr]);
-    const f32x4 bo = *reinterpret_cast<const f32x4*>(&s_b[P][ln][4 * lr]);
-    f32x4 xb[4], cb[4];
+    // (Delta*log2(e), x) of timestep ln for this lane's channel; B and C of its state
+    const float2 sdx = s_dx[P][ln][cr];
+    const float sd = sdx.x, sx = sdx.y;
+    f32x4 bb[4], cb[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      // xb[m][v] = x[4m + v][channel] * B[4m + v][state] for this lane
-      xb[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[m], bo[m], zero4, 0, 0, 0);
+      bb[m] = *reinterpret_cast<const f32x4*>(&s_b[P][ln][4 * m]);
       if constexpr (OUT) cb[m] = *reinterpret_cast<const f32x4*>(&s_c[P][ln][4 * m]);
     }
     float pg = 0.f, pd = 0.f;
@@ -349,7 +336,7 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
         constexpr int t = decltype(tc)::value;
         if constexpr (t % kBwdBlock == 0) checkpoint(pc, t / kBwdBlock);
         const float e = hw_exp2(row_bcast<t>(sd) * Av);
-        const float xbt = xb[t >> 2][t & 3];
+        const float xbt = row_bcast<t>(sx) * bb[t >> 2][t & 3];   // x_t B_t[n]
         if constexpr (EULER) {
           h = fmaf(e, h, xbt);
         } else {
@@ -370,7 +357,7 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
         const float e = hw_exp2(dl2 * Av);
         const float gz = (e - 1.f) * rA, g0 = dl2 * kLn2;
         const float g = (Av != 0.f) ? gz : g0;
-        h = fmaf(e, h, g * xb[t >> 2][t & 3]);
+        h = fmaf(e, h, g * (row_bcast<t>(sx) * bb[t >> 2][t & 3]));
         if constexpr (OUT) p[t] = cb[t >> 2][t & 3] * h;
       });
     }
@@ -378,8 +365,7 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
     __syncthreads();
   };
 
-  // zero once: the zero row of the x staging, and the B/C rows of states past N
-  if (threadIdx.x < 2 * XR) s_xt[threadIdx.x / XR][kTile][threadIdx.x % XR] = 0.f;
+  // zero once: the B/C rows of states past N (never written afterwards)
   for (int i = threadIdx.x; i < 2 * 16 * BR; i += 1024) {
     (&s_b[0][0][0])[i] = 0.f;
     if constexpr (OUT) (&s_c[0][0][0])[i] = 0.f;
