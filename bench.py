@@ -37,7 +37,8 @@ OPS_PER_TOKEN_CHANNEL = 20   # softplus 11, silu 7, skip + gate 2
 PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "sscan_fwd_train_shape_counters.json")
 COPY_ELEMS = 128 << 20                       # calibration copy: 512 MiB of fp32
 KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_45_amd", "csrc", f)
-                  for f in ("sscan_fwd_row.h", "sscan_fwd_row_zoh.hip", "sscan_device.h", "sscan_internal.h")]
+                  for f in ("sscan_fwd_row.h", "sscan_fwd_row_zoh.hip", "sscan_lanes.h", "sscan_device.h",
+                            "sscan_internal.h")]
 
 
 def kernel_source_hash() -> str:
