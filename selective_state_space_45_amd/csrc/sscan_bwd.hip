@@ -40,6 +40,7 @@
 #include "selscan.h"
 #include "sscan_device.h"
 #include "sscan_internal.h"
+#include "sscan_lanes.h"
 
 namespace sscan {
 
@@ -635,6 +636,161 @@ __global__ __launch_bounds__(NW * 64) void bwd_agg_kernel(
   }
 }
 
+// The same reverse aggregates for N == 16 with the forward's row layout: 16 waves,
+// wave w owning channels 4w .. 4w+3 (one per 16-lane row) and lane n of a row owning
+// state n.  Chunks of 16 steps are staged as above (wave w stages timestep w of the
+// chunk, lane = channel) and consumed last chunk first.  Lane t of a row reads its
+// channel's (Delta*log2(e), gyo) of timestep t once per chunk, and the DPP row
+// broadcast hands timestep t's pair to the whole row, folded into the multiplies by A
+// and by C; C of the lane's state comes as four 128-bit reads per chunk.  Per step and
+// state: G <- exp2(Delta*log2(e) A) (gyo C + G), five VALU and no LDS access, against
+// four VALU and two LDS reads with one state per wave.
+template <typename Tin>
+__global__ __launch_bounds__(1024) void bwd_agg_row_kernel(
+    const Tin* __restrict__ dtg, const Tin* __restrict__ zg, const Tin* __restrict__ Cg,
+    const Tin* __restrict__ dyg, const float* __restrict__ Ag, const float* __restrict__ biasg,
+    float* __restrict__ ragg_g, float* __restrict__ ragg_s, BwdShape sh) {
+  constexpr int T = 16, N = 16;
+  constexpr int DP = kTile + 1;   // row stride 130 words: 2 mod 32
+  constexpr int BR = T + 4;       // [state][timestep] rows of 20 words
+  __shared__ float2 s_dg[2][T][DP];
+  __shared__ __align__(16) float s_c[2][N][BR];
+  __shared__ float s_sum[16][kTile];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ln = lane & 15, lr = lane >> 4;
+  int64_t blk = xcd_remap(blockIdx.x, sh.ndtiles * sh.batch * (sh.nseg - 1));
+  const int64_t dtile = blk % sh.ndtiles;
+  blk /= sh.ndtiles;
+  const int64_t b = blk % sh.batch;
+  const int seg = static_cast<int>(blk / sh.batch) + 1;
+  const int64_t L = sh.L, dim = sh.dim;
+  // staging: lane = channel (clamped to an in-range one past dim)
+  const int64_t d = dtile * kTile + lane;
+  const bool dvalid = d < dim;
+  const int64_t dd = dvalid ? d : dim - 1;
+  const unsigned dlane = static_cast<unsigned>(dd - dtile * kTile) * sizeof(Tin);
+  // recurrence: lane = (state ln, channel 4w + lr)
+  const int cr = 4 * w + lr;
+  const int64_t dr = dtile * kTile + cr;
+  const bool drvalid = dr < dim;
+  const int64_t drc = drvalid ? dr : dim - 1;
+  const bool hasZ = zg != nullptr;
+  const float bias2 = biasg ? biasg[dd] * kLog2e : 0.f;
+  const float Av = Ag[drc * N + ln];
+
+  const int64_t l_beg = static_cast<int64_t>(seg) * sh.seg_blocks * kBwdBlock;
+  const int64_t l_end = (l_beg + sh.seg_blocks * kBwdBlock < L) ? l_beg + sh.seg_blocks * kBwdBlock : L;
+  const int seg_n = static_cast<int>(l_end - l_beg);
+  const int nch = (seg_n + T - 1) / T;
+  const int64_t tok = (b * L + l_beg) * dim + dtile * kTile;
+  const Tin* __restrict__ DTb = dtg + tok;
+  const Tin* __restrict__ DYb = dyg + tok;
+  const Tin* __restrict__ Zb = hasZ ? zg + tok : dtg + tok;
+  // C staging: waves 0-7 stage rows 2w and 2w+1 of the chunk, lane j*16 + n state n
+  // (waves 8-15 load the same rows and discard them)
+  const bool cwave = w < 8;
+  const int crow = 2 * (w & 7) + ((lane >> 4) & 1);
+  const int cn = lane & 15;
+  const Tin* __restrict__ Cs = Cg + (b * L + l_beg) * N;
+
+  float G = 0.f;
+  float ssum = 0.f, scomp = 0.f;   // Kahan sum of the staged Delta*log2(e) (lane = channel)
+  // Two register sets of loaded inputs: a chunk's loads are issued two iterations
+  // before it is staged, so that their latency is hidden behind two chunks of steps.
+  Tin r_dt[2], r_z[2], r_dy[2], r_c[2];
+  // loads of chunk c into set S; positions past the segment end read its last row
+  // (those steps become identities in the staging)
+  auto gload = [&](auto sc, int c) {
+    constexpr int S = decltype(sc)::value;
+    const int l = c * T + w;
+    const int64_t off = static_cast<int64_t>(l < seg_n ? l : seg_n - 1) * dim;
+    r_dt[S] = ld_off(DTb + off, dlane);
+    r_dy[S] = ld_off(DYb + off, dlane);
+    r_z[S] = ld_off(Zb + off, dlane);
+    const int t = c * T + crow;
+    r_c[S] = Cs[static_cast<int64_t>(t < seg_n ? t : seg_n - 1) * N + cn];
+  };
+  // stage chunk c from register set S into LDS buffer P
+  auto stage = [&](auto pc, auto sc, int c) {
+    constexpr int P = decltype(pc)::value;
+    constexpr int S = decltype(sc)::value;
+    const bool lv = c * T + w < seg_n;
+    const float gy = to_f32(r_dy[S]);
+    const float go = hasZ ? gy * silu(to_f32(r_z[S])) : gy;
+    const float d2 = lv ? softplus_log2e(fmaf(to_f32(r_dt[S]), kLog2e, bias2)) : 0.f;
+    s_dg[P][w][lane] = make_float2(d2, lv ? go : 0.f);
+    const float yk = d2 - scomp;   // padded steps add 0
+    const float tk = ssum + yk;
+    scomp = (tk - ssum) - yk;
+    ssum = tk;
+    // lanes that stage no C element store into their s_sum slot instead (written for
+    // real only after the last chunk), so that no store here runs under a partial
+    // exec mask near the DPP broadcasts
+    float* cdst = (cwave && lane < 2 * N) ? &s_c[P][cn][crow] : &s_sum[w][lane];
+    *cdst = (c * T + crow < seg_n) ? to_f32(r_c[S]) : 0.f;
+  };
+  // Processing step j handles chunk c = nch-1-j from LDS buffer j&1, stages chunk
+  // c-1 (loaded into set (j+1)&1) into the other buffer and loads chunk c-3 into the
+  // set just freed.  STEADY: c >= 3, so all of it exists and needs no branch.
+  auto iteration = [&](auto pc, auto steadyc, int c) {
+    constexpr int P = decltype(pc)::value;
+    constexpr int Q = 1 - P;
+    constexpr bool STEADY = decltype(steadyc)::value;
+    const float2 sdg = s_dg[P][ln][cr];
+    const float sd = sdg.x, sg = sdg.y;
+    f32x4 cb[4];
+    auto read_c = [&](int m) { cb[m] = *reinterpret_cast<const f32x4*>(&s_c[P][ln][4 * m]); };
+    read_c(3);
+    if (STEADY || c > 0) {
+      stage(Par<Q>{}, Par<Q>{}, c - 1);
+      if (STEADY || c > 2) gload(Par<Q>{}, c - 3);
+    }
+    static_for<0, T>([&](auto ic) {
+      constexpr int t = T - 1 - decltype(ic)::value;
+      if constexpr (t == 15 || t == 12 || t == 9) {
+        __builtin_amdgcn_sched_barrier(0);
+        read_c((t - 9) / 3);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const float e = hw_exp2(row_bcast<t>(sd) * Av);
+      const float gc = row_bcast<t>(sg) * cb[t >> 2][t & 3];
+      G = e * (gc + G);
+    });
+    __syncthreads();
+  };
+  if (nch > 0) {
+    gload(Par<0>{}, nch - 1);
+    stage(Par<0>{}, Par<0>{}, nch - 1);
+    if (nch > 1) gload(Par<1>{}, nch - 2);
+    if (nch > 2) gload(Par<0>{}, nch - 3);
+    __syncthreads();
+    // buffer and register-set parities follow the processing order, so they stay
+    // compile-time constants
+    int c = nch - 1;
+    for (; c >= 4; c -= 2) {
+      iteration(Par<0>{}, std::true_type{}, c);
+      iteration(Par<1>{}, std::true_type{}, c - 1);
+    }
+    for (; c >= 1; c -= 2) {
+      iteration(Par<0>{}, std::false_type{}, c);
+      iteration(Par<1>{}, std::false_type{}, c - 1);
+    }
+    if (c == 0) iteration(Par<0>{}, std::false_type{}, 0);
+  }
+  s_sum[w][lane] = ssum;
+  __syncthreads();
+  const int64_t rowbase = static_cast<int64_t>(seg) * sh.batch + b;
+  if (drvalid) ragg_g[(rowbase * dim + dr) * N + ln] = G;
+  if (w == 0 && dvalid) {
+    float sum = 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) sum += s_sum[q][lane];
+    ragg_s[rowbase * dim + d] = sum;
+  }
+}
+
 // gin[s] = gradient entering the end of segment s: gin[nseg-1] = dLoss/d(last state)
 // (or 0), gin[s-1] = exp2(A * sum_s) * gin[s] + ragg_g[s].
 __global__ __launch_bounds__(256) void bwd_carry_kernel(const float* __restrict__ ragg_g,
@@ -708,14 +864,20 @@ template <typename Tin, int NW, int NF, bool EU>
 void launch_bwd_one(const BwdParams& p, hipStream_t s) {
   BwdShape sh{p.batch, p.L, p.dim, p.ndtiles, p.nblk, p.seg_blocks, p.N, p.nseg};
   if (p.nseg > 1) {
-    // one state per wave in the aggregate pass: twice the reverse pass's waves, for
-    // occupancy (measured: two states per wave was no faster on the training shape)
-    constexpr int AS = 1;
-    constexpr int AW = NW * kBwdSpw / AS;
-    hipLaunchKernelGGL((bwd_agg_kernel<Tin, AW, AS, NF>), dim3(static_cast<unsigned>(p.ndtiles * p.batch * (p.nseg - 1))),
-                       dim3(AW * 64), 0, s, static_cast<const Tin*>(p.dt), static_cast<const Tin*>(p.z),
-                       static_cast<const Tin*>(p.C), static_cast<const Tin*>(p.dy), p.A, p.bias, p.ragg_g, p.ragg_s,
-                       sh);
+    const dim3 agrid(static_cast<unsigned>(p.ndtiles * p.batch * (p.nseg - 1)));
+    if constexpr (NF == 16) {
+      hipLaunchKernelGGL((bwd_agg_row_kernel<Tin>), agrid, dim3(1024), 0, s, static_cast<const Tin*>(p.dt),
+                         static_cast<const Tin*>(p.z), static_cast<const Tin*>(p.C), static_cast<const Tin*>(p.dy),
+                         p.A, p.bias, p.ragg_g, p.ragg_s, sh);
+    } else {
+      // one state per wave in the aggregate pass: twice the reverse pass's waves, for
+      // occupancy (measured: two states per wave was no faster on the training shape)
+      constexpr int AS = 1;
+      constexpr int AW = NW * kBwdSpw / AS;
+      hipLaunchKernelGGL((bwd_agg_kernel<Tin, AW, AS, NF>), agrid, dim3(AW * 64), 0, s, static_cast<const Tin*>(p.dt),
+                         static_cast<const Tin*>(p.z), static_cast<const Tin*>(p.C), static_cast<const Tin*>(p.dy),
+                         p.A, p.bias, p.ragg_g, p.ragg_s, sh);
+    }
     const int64_t total = p.batch * p.dim * p.N;
     hipLaunchKernelGGL(bwd_carry_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s,
                        p.ragg_g, p.ragg_s, p.A, p.dlast, p.gin, p.batch, p.dim, p.N, p.nseg);

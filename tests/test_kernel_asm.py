@@ -1,4 +1,4 @@
-"""Static checks on the gfx950 assembly of the row-layout forward kernel (CPU only:
+"""Static checks on the gfx950 assembly of the row-layout kernels (CPU only:
 hipcc cross-compiles; nothing runs on a GPU).
 
 A DPP read takes its value from another lane.  If that lane is switched off in the
@@ -86,3 +86,19 @@ def test_row_kernel_dpp_runs_with_full_rows(tmp_path):
     for name, (total, masked) in res.items():
         assert total >= 16, (name, total)     # at least the 16 row broadcasts of a chunk
         assert masked == 0, "%s: %d DPP instructions inside an exec-masked block" % (name, masked)
+
+
+@pytest.mark.skipif(_hipcc() is None, reason="hipcc not found")
+def test_backward_dpp_runs_with_full_rows(tmp_path):
+    # bwd_agg_row_kernel broadcasts (Delta, gyo) across each row the same way, and
+    # bwd_kernel reduces across lanes with DPP; neither may do so under an exec mask
+    asm = _compile_asm("sscan_bwd.hip", str(tmp_path / "bwd.s"))
+    agg = dpp_under_partial_exec(asm, r"_ZN5sscan18bwd_agg_row_kernel\w+")
+    assert len(agg) == 2, sorted(agg)   # bf16 and fp32
+    for name, (total, masked) in agg.items():
+        assert total >= 32, (name, total)   # two broadcasts per step of a chunk
+        assert masked == 0, "%s: %d DPP instructions inside an exec-masked block" % (name, masked)
+    rev = dpp_under_partial_exec(asm, r"_ZN5sscan10bwd_kernel\w+")
+    assert len(rev) == 20, sorted(rev)
+    for name, (total, masked) in rev.items():
+        assert total > 0 and masked == 0, (name, total, masked)
