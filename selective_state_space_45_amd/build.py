@@ -9,7 +9,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libselscan.so")
 SOURCES = ["csrc/sscan_api.hip", "csrc/sscan_fwd.hip", "csrc/sscan_fwd_zoh.hip", "csrc/sscan_fwd_euler.hip",
-           "csrc/sscan_fwd_row_zoh.hip", "csrc/sscan_fwd_row_euler.hip", "csrc/sscan_fwd_conv.hip",
+           "csrc/sscan_fwd_row_zoh.hip", "csrc/sscan_fwd_row_euler.hip", "csrc/sscan_fwd_row_conv.hip",
+           "csrc/sscan_fwd_conv.hip",
            "csrc/sscan_step.hip", "csrc/sscan_bwd.hip"]
 
 # Packed-FP32 instructions are disabled on purpose: the VALU code is written for

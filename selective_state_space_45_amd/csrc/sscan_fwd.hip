@@ -23,6 +23,8 @@ extern template hipError_t launch_fwd_row<kFwdOutCkpt, false>(const FwdParams&, 
 extern template hipError_t launch_fwd_row<kFwdOut, true>(const FwdParams&, bool, hipStream_t);
 extern template hipError_t launch_fwd_row<kFwdCkpt, true>(const FwdParams&, bool, hipStream_t);
 extern template hipError_t launch_fwd_row<kFwdOutCkpt, true>(const FwdParams&, bool, hipStream_t);
+extern template hipError_t launch_fwd_row<kFwdOutConv, false>(const FwdParams&, bool, hipStream_t);
+extern template hipError_t launch_fwd_row<kFwdOutConv, true>(const FwdParams&, bool, hipStream_t);
 
 // carry[s] = state entering segment s: carry[0] = h_init (or 0),
 // carry[s+1] = exp2(A * S_s) * carry[s] + hend_s, where S_s is the segment's sum of
@@ -53,11 +55,11 @@ __global__ __launch_bounds__(256) void fill_state_kernel(float* __restrict__ dst
   if (i < n) dst[i] = src ? src[i] : 0.f;
 }
 
-// Launches taken by the row layout (fwd_row_kernel): N <= 16, no convolution prologue,
-// and one workgroup per CU at a time (the one-state-per-wave grids).  Measured on the
+// Launches taken by the row layout (fwd_row_kernel): N <= 16 and one workgroup per CU
+// at a time (the one-state-per-wave grids), with or without the convolution prologue.  Measured on the
 // training shape (batch 8, seqlen 4096, dim 2048, N 16, bf16), steady state: 0.40 ms
 // against 0.45 for fwd_kernel with one state per wave; Euler rule 0.35 against 0.43.
-bool fwd_row_layout(const FwdParams& p) { return p.N <= 16 && !p.conv_w && p.npw == 1; }
+bool fwd_row_layout(const FwdParams& p) { return p.N <= 16 && p.npw == 1; }
 
 // Waves per workgroup: N / (states per wave) rounded up to a power of two (at most 16).
 int fwd_nsplit(int npw, int N) {
@@ -73,9 +75,15 @@ namespace {
 template <int MODE>
 hipError_t launch_fwd_mode(const FwdParams& p, bool bf16, hipStream_t s) {
   if constexpr (MODE == kFwdOut || MODE == kFwdAgg) {   // the modes with a convolution prologue
-    if (p.conv_w)
+    if (p.conv_w) {
+      if constexpr (MODE == kFwdOut) {
+        if (fwd_row_layout(p))
+          return p.euler ? launch_fwd_row<kFwdOutConv, true>(p, bf16, s)
+                         : launch_fwd_row<kFwdOutConv, false>(p, bf16, s);
+      }
       return p.euler ? launch_fwd_variant<MODE, true, true>(p, bf16, s)
                      : launch_fwd_variant<MODE, false, true>(p, bf16, s);
+    }
   }
   if constexpr (MODE != kFwdAgg) {
     // the checkpoint pass always runs one state per wave, hence the row layout

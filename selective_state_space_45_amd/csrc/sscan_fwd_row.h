@@ -104,17 +104,24 @@ __device__ __forceinline__ float row_reduce_scatter16(const float (&p)[16], int 
 
 // One workgroup: (batch row b, 64-channel tile, segment); 16 waves x 4 channels x 16
 // states.  MODE: kFwdOut (y and the final state), kFwdCkpt (no y: the state entering
-// every block of kBwdBlock steps, for the backward pass), kFwdOutCkpt (both).
+// every block of kBwdBlock steps, for the backward pass), kFwdOutCkpt (both),
+// kFwdOutConv (kFwdOut on the output of the convolution prologue: x is the raw input
+// of a causal depthwise conv1d over time, conv_w [dim][dconv] taps and optional
+// conv_b [dim], followed by SiLU, as in the page-3 report's MambaBlock (section 3,
+// forward); inputs before the sequence start come from conv_s [batch][dim][dconv-1],
+// zeros when absent).
 // NFIX: N as a compile-time constant (16) or 0 (from the shape, N <= 16).
 template <typename Tin, int MODE, int NFIX, bool EULER>
 __global__ __launch_bounds__(1024) void fwd_row_kernel(
     const Tin* __restrict__ xg, const Tin* __restrict__ dtg, const Tin* __restrict__ zg,
     const Tin* __restrict__ Bg, const Tin* __restrict__ Cg, const float* __restrict__ Ag,
     const float* __restrict__ Dg, const float* __restrict__ biasg, const float* __restrict__ h_init,
-    Tin* __restrict__ yg, float* __restrict__ h_last, float* __restrict__ ckpt, FwdShape sh) {
-  constexpr bool OUT = MODE == kFwdOut || MODE == kFwdOutCkpt;
+    Tin* __restrict__ yg, float* __restrict__ h_last, float* __restrict__ ckpt, const float* __restrict__ conv_w,
+    const float* __restrict__ conv_b, const float* __restrict__ conv_s, FwdShape sh) {
+  constexpr bool CONV = MODE == kFwdOutConv;
+  constexpr bool OUT = MODE == kFwdOut || MODE == kFwdOutCkpt || CONV;
   constexpr bool CKPT = MODE == kFwdCkpt || MODE == kFwdOutCkpt;
-  static_assert(MODE == kFwdOut || CKPT, "output and checkpoint modes");
+  static_assert(MODE == kFwdOut || CKPT || CONV, "output, checkpoint and convolution modes");
   constexpr int T = kChunk;
   static_assert(T == 16, "one staged timestep per lane of a row");
   static_assert(!CKPT || 2 * kBwdBlock == T, "checkpoints are taken at half chunks");
@@ -193,7 +200,20 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
   float h = 0.f;
   if (h_init && drvalid && nlive) h = h_init[((static_cast<int64_t>(seg) * sh.batch + b) * dim + dr) * N + ln];
 
+  // CONV: taps and bias of this lane's channel; taps past dconv are zero
+  constexpr int KC = CONV ? kMaxConv : 1;
+  const int K = CONV ? sh.dconv : 1;
+  float cw[KC];
+  float cbias = 0.f;
+  if constexpr (CONV) {
+#pragma unroll
+    for (int k = 0; k < KC; ++k) cw[k] = (k < K) ? conv_w[dd * K + k] : 0.f;
+    cbias = conv_b ? conv_b[dd] : 0.f;
+  }
+  const Tin* __restrict__ Xrow = xg + b * L * dim + dtile * kTile;   // whole sequence of this row
+
   Tin rx, rdt, rz, rbc;
+  Tin rxc[KC];
   // Global loads of chunk c for the prologue: x, dt, z of timestep w (lane = channel)
   // and this wave's B/C rows.  STEADY: chunk c is full.  Otherwise positions past the
   // segment end read its last row (those steps become identities in the prologue).
@@ -201,7 +221,19 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
     constexpr bool STEADY = decltype(steadyc)::value;
     const int l = c * T + w;
     const int64_t off = static_cast<int64_t>(STEADY ? l : (l < seg_n ? l : seg_n - 1)) * dim;
-    rx = ld_off(Xb + off, dlane);
+    if constexpr (CONV) {
+      // raw inputs of the window l - (K-1) .. l, from positions clamped at the sequence
+      // start (replaced from conv_s in the prologue); taps past K load position l
+      const int64_t lg = l_begin + (STEADY ? l : (l < seg_n ? l : seg_n - 1));
+#pragma unroll
+      for (int k = 0; k < KC; ++k) {
+        const int back = (K - 1 - k) < 0 ? 0 : (K - 1 - k);
+        const int64_t pos = lg - (back <= lg ? back : lg);
+        rxc[k] = ld_off(Xrow + pos * dim, dlane);
+      }
+    } else {
+      rx = ld_off(Xb + off, dlane);
+    }
     rdt = ld_off(DTb + off, dlane);
     if constexpr (OUT) rz = ld_off(Zb + off, dlane);
     if (bcwave) {
@@ -218,7 +250,26 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
   auto prologue = [&](auto pc, auto steadyc, int c) {
     constexpr int P = decltype(pc)::value;
     constexpr bool STEADY = decltype(steadyc)::value;
-    float xv = to_f32(rx);
+    float xv;
+    if constexpr (CONV) {
+      const int64_t l_glob = l_begin + c * T + w;
+      float v[KC];
+#pragma unroll
+      for (int k = 0; k < KC; ++k) v[k] = to_f32(rxc[k]);
+      if (l_glob < K - 1) {   // wave-uniform: the window reaches before the sequence
+#pragma unroll
+        for (int k = 0; k < KC; ++k) {
+          const int64_t pos = l_glob - (K - 1) + k;
+          if (pos < 0) v[k] = (conv_s && dvalid) ? conv_s[(b * dim + d) * (K - 1) + (K - 1) + pos] : 0.f;
+        }
+      }
+      float acc = cbias;
+#pragma unroll
+      for (int k = 0; k < KC; ++k) acc = fmaf(cw[k], v[k], acc);
+      xv = silu(acc);
+    } else {
+      xv = to_f32(rx);
+    }
     float d2 = softplus_log2e(fmaf(to_f32(rdt), kLog2e, bias2));
     if constexpr (!STEADY) {   // a padded step is the identity: Delta = 0, x = 0
       const bool lv = c * T + w < seg_n;
@@ -387,7 +438,7 @@ void launch_row_one(const FwdParams& p, dim3 grid, hipStream_t s) {
   hipLaunchKernelGGL((fwd_row_kernel<Tin, MODE, NF, EU>), grid, dim3(1024), 0, s, static_cast<const Tin*>(p.x),
                      static_cast<const Tin*>(p.dt), static_cast<const Tin*>(p.z), static_cast<const Tin*>(p.B),
                      static_cast<const Tin*>(p.C), p.A, p.Dskip, p.bias, p.h_init, static_cast<Tin*>(p.y), p.h_last,
-                     p.ckpt, sh);
+                     p.ckpt, p.conv_w, p.conv_b, p.conv_s, sh);
 }
 
 // Launch of one (mode, discretization rule) variant of the row layout (N <= 16).

@@ -16,6 +16,7 @@ constexpr int kFwdOut = 0;    // y (and the final state)
 constexpr int kFwdAgg = 1;    // per-segment aggregates for the two-level scan
 constexpr int kFwdCkpt = 2;   // states entering every kBwdBlock steps, for the backward pass
 constexpr int kFwdOutCkpt = 3;  // y and the final state, and the kFwdCkpt states as well
+constexpr int kFwdOutConv = 4;  // kFwdOut with the convolution prologue (row layout only)
 
 struct FwdParams {
   const void* x;

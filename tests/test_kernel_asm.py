@@ -102,3 +102,15 @@ def test_backward_dpp_runs_with_full_rows(tmp_path):
     assert len(rev) == 20, sorted(rev)
     for name, (total, masked) in rev.items():
         assert total > 0 and masked == 0, (name, total, masked)
+
+
+@pytest.mark.skipif(_hipcc() is None, reason="hipcc not found")
+def test_row_kernel_conv_dpp_runs_with_full_rows(tmp_path):
+    # the convolution-prologue variants: the prologue's branch for windows that reach
+    # before the sequence start must not take the recurrence's broadcasts with it
+    asm = _compile_asm("sscan_fwd_row_conv.hip", str(tmp_path / "row_conv.s"))
+    res = dpp_under_partial_exec(asm, r"_ZN5sscan14fwd_row_kernel\w+")
+    assert len(res) == 8, sorted(res)   # both rules, bf16 and fp32, N = 16 and any N
+    for name, (total, masked) in res.items():
+        assert total >= 16, (name, total)
+        assert masked == 0, "%s: %d DPP instructions inside an exec-masked block" % (name, masked)
