@@ -504,7 +504,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(
 // reverse recurrence G <- Abar (gyo C + G) run over the segment from G = 0 at its end
 // gives the gradient its steps send to the state before its start (ragg_g); with the
 // segment's sum of Delta*log2(e) (ragg_s), exp2(A * sum) is the product of Abar over
-// it.  A workgroup per (batch row, channel tile, segment) with AS states per wave;
+// it.  For N != 16 (N == 16 runs bwd_agg_row_kernel below): a workgroup per (batch
+// row, channel tile, segment) with AS states per wave;
 // blocks of kAggBlock steps staged through LDS, double-buffered so that the staging
 // of the next block overlaps the steps of this one, with one barrier per block.
 constexpr int kAggBlock = 32;

@@ -115,7 +115,8 @@ __device__ __forceinline__ int64_t after(int64_t v, float dep) {
 // block of kBwdBlock steps is written to ckpt, for the backward pass), kFwdOutCkpt
 // (both kFwdOut's and kFwdCkpt's outputs).  Launched are: the two-states-per-wave
 // main pass of split grids (kFwdOut, kFwdOutCkpt), the aggregate pass, and the
-// convolution prologue; the other launches run fwd_row_kernel (sscan_fwd_row.h).
+// convolution prologue of split grids; the other launches run fwd_row_kernel
+// (sscan_fwd_row.h).
 // NFIX: N as a compile-time constant (0 = read it from the shape at run time).
 // EULER: Bbar = Delta B instead of the zero-order hold.
 // CONV: x is the raw input of a causal depthwise convolution over time (sh.dconv
@@ -582,9 +583,9 @@ void launch_by_n(const FwdParams& p, dim3 grid, hipStream_t s) {
     }
     return;
   }
-  // One state per wave: only the aggregate pass and the convolution prologue still
-  // take it (other one-state launches run fwd_row_kernel; launch_fwd_variant rejects
-  // them here).
+  // One state per wave: only the aggregate pass and the convolution prologue of split
+  // grids with N < 3 still take it (other one-state launches run fwd_row_kernel;
+  // launch_fwd_variant rejects them here).
   if constexpr (MODE == kFwdAgg || CV) {
     switch (fwd_nsplit(1, p.N)) {
       case 1: launch_one<Tin, 1, 1, MODE, PR, 0, EU, CV>(p, grid, s); break;
