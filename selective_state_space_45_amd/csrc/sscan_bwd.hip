@@ -315,6 +315,13 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(
 #pragma unroll
     for (int q = 0; q < S; ++q) h[q] = h_next[q];
     __syncthreads();
+    // this wave's B and C pairs of the block, addressed from a vector register (a zero
+    // the compiler cannot see through), so that the per-step reads use immediate
+    // offsets instead of re-copying a scalar address into a vector register each step
+    int vzero;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(vzero));
+    const VS* __restrict__ sBw = reinterpret_cast<const VS*>(reinterpret_cast<const char*>(&s_B[pb][0][w]) + vzero);
+    const VS* __restrict__ sCw = reinterpret_cast<const VS*>(reinterpret_cast<const char*>(&s_C[pb][0][w]) + vzero);
 
     // ---- P2: recompute the block's states from the checkpoint; partial C.h of the
     // readout to LDS; terms of dC summed across lanes ----
@@ -330,8 +337,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(
           const float xv = s_xv[pb][t][lane];
           const float go = s_go[pb][t][lane];
           float bq[S], cq[S];
-          unpack(s_B[pb][t][w], bq);
-          unpack(s_C[pb][t][w], cq);
+          unpack(sBw[t * (NSP / S)], bq);
+          unpack(sCw[t * (NSP / S)], cq);
           float yo = 0.f;
 #pragma unroll
           for (int q = 0; q < S; ++q) {
@@ -376,8 +383,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(
         const float d2 = s_d2[pb][t][lane];
         const float xv = s_xv[pb][t][lane];
         float bq[S], cq[S];
-        unpack(s_B[pb][t][w], bq);
-        unpack(s_C[pb][t][w], cq);
+        unpack(sBw[t * (NSP / S)], bq);
+        unpack(sCw[t * (NSP / S)], cq);
         const float delta = d2 * kLn2;
         float r1 = 0.f, r2 = 0.f;
 #pragma unroll
@@ -388,39 +395,39 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(
           const float bx = bq[q] * xv;
           // hn = h_l, the state after the step: h_l = Abar h_{l-1} + phi B x
           const float hn = (t + 1 < T) ? hist[q][t + 1] : h[q];
-          float gphi, Gn;
+          float gphi;
+          const float Gn = a * gh;
           if constexpr (EULER) {
             gphi = gh * delta;
-            Gn = a * gh;
             r2 = fmaf(gh, fmaf(An[q] * a, hp, bx), r2);
             gA[q] = fmaf(gh, delta * a * hp, gA[q]);
-          } else if (!zeroA) {
-            // d h_l / d Delta = Abar (A h_{l-1} + B x) = A hn + B x, and
-            // d h_l / d A = Delta Abar (h_{l-1} + k) - phi k = Delta (hn + k) - phi k
-            // with k = B x / A; gh phi = (Abar gh - gh) / A, so phi is never formed.
-            // The term (Delta Abar - phi) k cancels for small Delta A, but only down to
-            // a few ulp of Delta k, the size of the leading term
-            Gn = a * gh;
-            gphi = (Gn - gh) * iAn[q];
-            r2 = fmaf(gh, fmaf(An[q], hn, bx), r2);
-            const float k = bx * iAn[q];
-            gA[q] = fmaf(delta, gh * (hn + k), gA[q]);
-            gA[q] = fmaf(-gphi, k, gA[q]);
           } else {
-            const float phi = (An[q] != 0.f) ? (a - 1.f) * iAn[q] : delta;
-            gphi = gh * phi;
-            Gn = a * gh;
+            // d h_l / d Delta = Abar (A h_{l-1} + B x) = A hn + B x in both cases, formed
+            // before the A = 0 branch so that the two branches share its registers
             r2 = fmaf(gh, fmaf(An[q], hn, bx), r2);
-            // a wave with some A == 0: dphi/dA = Delta^2 (u e^u - e^u + 1)/u^2, u = Delta A,
-            // from its series for |u| < 0.5 and its closed form otherwise; both are
-            // computed (each finite everywhere) and blended, so no per-lane branch
-            // splits the step
-            const float u = delta * An[q];
-            const float ser = delta * delta * dphi1_series(fmaxf(fminf(u, 0.5f), -0.5f));
-            const float dir = (delta * a - phi) * iAn[q];
-            const float wsel = (fabsf(u) < 0.5f) ? 1.f : 0.f;
-            const float dphi_dA = fmaf(wsel, ser - dir, dir);
-            gA[q] = fmaf(gh, fmaf(delta * a, hp, dphi_dA * bx), gA[q]);
+            if (!zeroA) {
+              // d h_l / d A = Delta Abar (h_{l-1} + k) - phi k = Delta (hn + k) - phi k
+              // with k = B x / A; gh phi = (Abar gh - gh) / A, so phi is never formed.
+              // The term (Delta Abar - phi) k cancels for small Delta A, but only down
+              // to a few ulp of Delta k, the size of the leading term
+              gphi = (Gn - gh) * iAn[q];
+              const float k = bx * iAn[q];
+              gA[q] = fmaf(delta, gh * (hn + k), gA[q]);
+              gA[q] = fmaf(-gphi, k, gA[q]);
+            } else {
+              const float phi = (An[q] != 0.f) ? (a - 1.f) * iAn[q] : delta;
+              gphi = gh * phi;
+              // a wave with some A == 0: dphi/dA = Delta^2 (u e^u - e^u + 1)/u^2,
+              // u = Delta A, from its series for |u| < 0.5 and its closed form
+              // otherwise; both are computed (each finite everywhere) and blended, so
+              // no per-lane branch splits the step
+              const float u = delta * An[q];
+              const float ser = delta * delta * dphi1_series(fmaxf(fminf(u, 0.5f), -0.5f));
+              const float dir = (delta * a - phi) * iAn[q];
+              const float wsel = (fabsf(u) < 0.5f) ? 1.f : 0.f;
+              const float dphi_dA = fmaf(wsel, ser - dir, dir);
+              gA[q] = fmaf(gh, fmaf(delta * a, hp, dphi_dA * bx), gA[q]);
+            }
           }
           red[q * T + t] = gphi * xv;
           r1 = fmaf(gphi, bq[q], r1);
