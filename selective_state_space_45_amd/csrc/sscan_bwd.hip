@@ -844,17 +844,18 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc(const float* __restrict__ g
 }
 
 // dA[d][n], dD[d], dbias[d] = sums over (segment, batch row) partials (fixed order).
+// One thread per (n, d), d fastest, so that the partial reads ([row][n][dim]) coalesce.
 __global__ __launch_bounds__(256) void bwd_reduce_params(const float* __restrict__ gAp, const float* __restrict__ gDp,
                                                          const float* __restrict__ gbp, float* __restrict__ dA,
                                                          float* __restrict__ dD, float* __restrict__ dbias,
                                                          int64_t rows, int64_t dim, int N) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;   // n * dim + d
   if (i >= dim * N) return;
-  const int64_t d = i / N;
-  const int n = static_cast<int>(i - d * N);
+  const int n = static_cast<int>(i / dim);
+  const int64_t d = i - static_cast<int64_t>(n) * dim;
   float s = 0.f;
-  for (int64_t r = 0; r < rows; ++r) s += gAp[(r * N + n) * dim + d];
-  dA[i] = s;
+  for (int64_t r = 0; r < rows; ++r) s += gAp[r * N * dim + i];
+  dA[d * N + n] = s;
   if (n == 0) {
     float sD = 0.f, sb = 0.f;
     for (int64_t r = 0; r < rows; ++r) {
