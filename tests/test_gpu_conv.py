@@ -103,3 +103,19 @@ def test_conv_prefill_then_decode(ss, orc, dtype):
     assert_close(np.concatenate(ys, axis=1), yr, tau, "y over prefill + decode")
     assert_close(host(st), sr, tau, "final scan state")
     np.testing.assert_array_equal(host(cst), cs_ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [7, 16])
+def test_conv_fwd_long_row_layout(ss, orc, dtype, N):
+    # L = 1000 over 2 x 100 channels: the sequence split gives segments of 9 chunks, each
+    # run through the row-layout kernel's steady loop, with convolution windows that
+    # reach back into the previous segment
+    w = W.make_scan_inputs(2, 1000, 100, N, dtype, seed=730 + N, name=f"conv long N={N}")
+    check_conv_fwd(ss, orc, w, 4, seed=31 + N)
+
+
+@pytest.mark.timeout(600)
+def test_conv_fwd_train_shape(ss, orc):
+    # one workgroup per CU, one segment: 256 chunks of the row-layout kernel
+    check_conv_fwd(ss, orc, W.workload("train_shape"), 4, seed=15)
