@@ -35,7 +35,7 @@
  *    checked on the host before any launch.  Values are not checked: NaN and
  *    Inf propagate.  SSCAN_ERR_HIP reports a failed launch.
  *  - Outputs must not overlap inputs, except where stated (in-place state).
- *  - dstate (N) must be in [1, SSCAN_MAX_DSTATE].
+ *  - dstate (N) must be in [1, SSCAN_MAX_DSTATE]; seqlen at most SSCAN_MAX_SEQLEN.
  *  - `flags` selects variants of the method (SSCAN_FLAG_*); 0 is the method
  *    as defined above.
  */
@@ -52,6 +52,10 @@ extern "C" {
 #define SSCAN_VERSION 410
 #define SSCAN_MAX_DSTATE 16
 #define SSCAN_MAX_DCONV 4
+/* Longest sequence sscan_fwd* and sscan_bwd* accept (2^30 steps): the kernels count
+ * the steps of one sequence segment in 32-bit integers.  Longer ones are rejected
+ * with SSCAN_ERR_INVALID_ARG. */
+#define SSCAN_MAX_SEQLEN (1LL << 30)
 
 /*
  * Bits of the `flags` argument.
@@ -87,7 +91,8 @@ const char* sscan_last_error(void);
  * scanned segments joined by a carry pass (a two-level scan over the sequence).
  * Returns 0 when the shape needs no split.  Pass at least this many bytes to
  * sscan_fwd to get the full split; fewer bytes give fewer segments (possibly
- * one), which is slower but equally correct.
+ * one), which is slower but equally correct.  The part of the workspace a call
+ * uses must not overlap any tensor of that call (SSCAN_ERR_INVALID_ARG).
  */
 size_t sscan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
                                 int dtype);

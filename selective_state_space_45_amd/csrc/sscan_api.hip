@@ -187,6 +187,9 @@ int fwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dty
   rc = check_conv(cv, batch, dim);
   if (rc) return rc;
   if (seqlen < 0) return fail(SSCAN_ERR_INVALID_ARG, "negative seqlen %lld", (long long)seqlen);
+  if (seqlen > SSCAN_MAX_SEQLEN)
+    return fail(SSCAN_ERR_INVALID_ARG, "seqlen %lld above SSCAN_MAX_SEQLEN (%lld)", (long long)seqlen,
+                (long long)SSCAN_MAX_SEQLEN);
   if (num_segments < 0) return fail(SSCAN_ERR_INVALID_ARG, "negative num_segments");
   const int64_t max_elems = (int64_t(1) << 62) / 8;
   if (batch > 0 && dim > 0 && seqlen > max_elems / batch / dim)
@@ -257,8 +260,19 @@ int fwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dty
   }
 
   const SegPlan pl = plan_segments(batch, seqlen, dim, N, num_segments, workspace_bytes, workspace != nullptr);
-  if (pl.nseg > 1 && overlaps(workspace, seg_workspace_bytes(batch, dim, N, pl.nseg), y, tok))
-    return fail(SSCAN_ERR_INVALID_ARG, "workspace overlaps y");
+  if (pl.nseg > 1) {
+    // the split writes its aggregates and carries into the workspace before the main
+    // pass reads the inputs, so the used part may overlap no tensor of the call
+    const size_t used = seg_workspace_bytes(batch, dim, N, pl.nseg);
+    const Buf others[] = {{x, tok}, {delta, tok}, {z, tok}, {y, tok}, {B, bc}, {C, bc},
+                          {A, static_cast<size_t>(N) * dim * 4}, {D, static_cast<size_t>(dim) * 4},
+                          {delta_bias, static_cast<size_t>(dim) * 4}, {initial_state, st}, {last_state, st},
+                          {cv.w, cv.w ? static_cast<size_t>(dim) * cv.dconv * 4 : 0},
+                          {cv.b, cv.b ? static_cast<size_t>(dim) * 4 : 0}, {cv.state_in, conv_bytes},
+                          {cv.state_out, conv_bytes}};
+    for (const Buf& o : others)
+      if (overlaps(workspace, used, o.p, o.n)) return fail(SSCAN_ERR_INVALID_ARG, "workspace overlaps a tensor");
+  }
 
   sscan::FwdParams p{};
   p.x = x; p.dt = delta; p.z = z; p.B = B; p.C = C;
@@ -371,6 +385,9 @@ int bwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dty
   int rc = check_common(batch, dim, dstate, dtype, flags);
   if (rc) return rc;
   if (seqlen < 0) return fail(SSCAN_ERR_INVALID_ARG, "negative seqlen %lld", (long long)seqlen);
+  if (seqlen > SSCAN_MAX_SEQLEN)
+    return fail(SSCAN_ERR_INVALID_ARG, "seqlen %lld above SSCAN_MAX_SEQLEN (%lld)", (long long)seqlen,
+                (long long)SSCAN_MAX_SEQLEN);
   const int64_t max_elems = (int64_t(1) << 62) / 8;
   if (batch > 0 && dim > 0 && seqlen > max_elems / batch / dim)
     return fail(SSCAN_ERR_INVALID_ARG, "batch*seqlen*dim too large");

@@ -15,7 +15,9 @@
 //   dA      = sum_{b,l} g_l (Delta Abar h_{l-1} + dphi/dA B_l x_l)
 // with phi = Bbar / B: (Abar - 1)/A for the zero-order hold (dphi/dDelta = Abar,
 // dphi/dA = (Delta Abar - phi)/A, evaluated by its Taylor series in u = Delta A when
-// |u| < 0.5), Delta for the Euler rule (dphi/dDelta = 1, dphi/dA = 0).
+// |u| < 0.5), Delta for the Euler rule (dphi/dDelta = 1, dphi/dA = 0).  Waves with some
+// |A| < kSmallA form phi itself with zoh_phi (accurate as u -> 0); the others use
+// forms that divide by A, exact in exact arithmetic and accurate for |A| >= kSmallA.
 //
 // Work decomposition: a workgroup owns (batch row, 64-channel tile, reverse
 // segment); lane = channel, and each wave owns kBwdSpw (two) states (a wave's sums
@@ -215,11 +217,14 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(
     const bool have = n0 + q < N;
     An[q] = have ? Ag[dd * N + n0 + q] : 0.f;
     iAn[q] = (An[q] != 0.f) ? 1.f / An[q] : 0.f;
-    anyzero = anyzero || (have && An[q] == 0.f);
+    anyzero = anyzero || (have && fabsf(An[q]) < kSmallA);
     G[q] = (g_in && have && dvalid) ? g_in[(b * dim + d) * N + n0 + q] : 0.f;
     gA[q] = 0.f;
   }
-  const bool zeroA = __any(dvalid && anyzero);
+  // wave-uniform: some state of the wave's channels has |A| < kSmallA (A == 0
+  // included), where the k-form's rounding error would matter; those waves take the
+  // explicit forms with the accurate zoh_phi
+  const bool smallA = __any(dvalid && anyzero);
 
   const int64_t tok_b = b * L * dim + dtile * kTile;  // token offset of (b, l = 0, this tile)
   float e_sig[TPW], e_gz[TPW];                       // epilogue values of this wave's timesteps
@@ -351,7 +356,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(
               const float k = xv * bq[q] * iAn[q];
               h[q] = fmaf(a, h[q] + k, -k);
             } else {
-              const float g = (An[q] != 0.f) ? (a - 1.f) * iAn[q] : d2 * kLn2;
+              const float g = zoh_phi(a, d2 * An[q], d2, iAn[q]);
               h[q] = fmaf(a, h[q], g * bq[q] * xv);
             }
             red[q * T + t] = go * h[q];
@@ -361,7 +366,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(
           __builtin_amdgcn_sched_barrier(0);
         }
       };
-      if (EULER || !zeroA)
+      if (EULER || !smallA)
         recompute(std::false_type{});
       else
         recompute(std::true_type{});
@@ -405,7 +410,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(
             // d h_l / d Delta = Abar (A h_{l-1} + B x) = A hn + B x in both cases, formed
             // before the A = 0 branch so that the two branches share its registers
             r2 = fmaf(gh, fmaf(An[q], hn, bx), r2);
-            if (!zeroA) {
+            if (!smallA) {
               // d h_l / d A = Delta Abar (h_{l-1} + k) - phi k = Delta (hn + k) - phi k
               // with k = B x / A; gh phi = (Abar gh - gh) / A, so phi is never formed.
               // The term (Delta Abar - phi) k cancels for small Delta A, but only down
@@ -415,9 +420,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(
               gA[q] = fmaf(delta, gh * (hn + k), gA[q]);
               gA[q] = fmaf(-gphi, k, gA[q]);
             } else {
-              const float phi = (An[q] != 0.f) ? (a - 1.f) * iAn[q] : delta;
+              const float phi = zoh_phi(a, d2 * An[q], d2, iAn[q]);
               gphi = gh * phi;
-              // a wave with some A == 0: dphi/dA = Delta^2 (u e^u - e^u + 1)/u^2,
+              // a wave with some small |A|: dphi/dA = Delta^2 (u e^u - e^u + 1)/u^2,
               // u = Delta A, from its series for |u| < 0.5 and its closed form
               // otherwise; both are computed (each finite everywhere) and blended, so
               // no per-lane branch splits the step

@@ -25,8 +25,8 @@
 //              staging then fits two workgroups in a CU's LDS.
 // The state update uses h <- Abar (h + k) - k with k = x B / A, which equals
 // Abar h + (Abar - 1) B x / A = Abar h + Bbar x: one add and one fma per state.
-// A wave whose channels have some A == 0 switches to the explicit form with the
-// Delta * B limit.  With the Euler rule (Bbar = Delta B, the page-3 report's code,
+// A wave whose channels have some |A| < kSmallA (A == 0 included) switches to the
+// explicit form h <- Abar h + phi B x with the accurate phi of zoh_phi (Delta at A = 0).  With the Euler rule (Bbar = Delta B, the page-3 report's code,
 // section 4.2) the prologue stages Delta*x instead of x and the update is
 // h <- Abar h + (Delta x) B.
 //
@@ -208,9 +208,10 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
     Aj[j] = have[j] ? Ag[dd * N + n0 + j] : 0.f;
     iAj[j] = (Aj[j] != 0.f) ? 1.f / Aj[j] : 0.f;
     live[j] = have[j] ? 1.f : 0.f;
-    anyzero = anyzero || (have[j] && Aj[j] == 0.f);
+    anyzero = anyzero || (have[j] && fabsf(Aj[j]) < kSmallA);
   }
-  const bool zeroA = __any(dvalid && anyzero);
+  // wave-uniform: some state of the wave's channels has |A| < kSmallA (A == 0 included)
+  const bool smallA = __any(dvalid && anyzero);
   // B of this wave: element (l, nbase + o) of the segment sits at Bw[l * N + o].
   const Tin* __restrict__ Bw = Bg + (b * L + l_begin) * N + nbase;
   // C rows of the segment (the epilogue reads whole rows).
@@ -365,8 +366,8 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
   };
 
   // One timestep of this wave's states, staged to LDS for the readout.  Fast form:
-  // h <- Abar (h + k) - k with k = x B / A.  Safe form (a wave with some A == 0):
-  // h <- Abar h + g B x with g = (Abar - 1)/A, or Delta when A == 0.
+  // h <- Abar (h + k) - k with k = x B / A.  Accurate form (a wave with some
+  // |A| < kSmallA): h <- Abar h + phi B x with phi = zoh_phi (Delta when A == 0).
   auto run_steps = [&](auto pc, auto hc, const float2* vx, const float (*ea)[NPW]) {
     constexpr int P = decltype(pc)::value;
     constexpr int HH = decltype(hc)::value;
@@ -381,7 +382,7 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
         }
         stage(pc, t);
       }
-    } else if (!zeroA) {
+    } else if (!smallA) {
 #pragma unroll
       for (int t = HH * H; t < (HH + 1) * H; ++t) {
 #pragma unroll
@@ -396,10 +397,9 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
     } else {
 #pragma unroll
       for (int t = HH * H; t < (HH + 1) * H; ++t) {
-        const float dl = vx[t].x * kLn2;
 #pragma unroll
         for (int j = 0; j < NPW; ++j) {
-          const float g = live[j] * ((Aj[j] != 0.f) ? (ea[t][j] - 1.f) * iAj[j] : dl);
+          const float g = live[j] * zoh_phi(ea[t][j], vx[t].x * Aj[j], vx[t].x, iAj[j]);
           h[j] = fmaf(ea[t][j], h[j], g * bc[t].get(j, sel) * vx[t].y);
           if constexpr (OUT && !PART) s_h[P][n0 + j][t][lane] = h[j];
         }

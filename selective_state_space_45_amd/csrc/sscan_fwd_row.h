@@ -32,7 +32,8 @@
 // states through LDS -- for DPP broadcasts and a register-only reduction; per wave and
 // chunk the LDS traffic drops from ~16 KB to ~9 KB, most of it 128-bit reads of B and C.
 // The state update is the same k-form: h <- Abar (h + k) - k with k = x B / A; a wave
-// whose channels have some A == 0 takes the explicit form, as a wave-uniform branch.
+// whose channels have some |A| < kSmallA (A == 0 included) takes the explicit form
+// with the accurate zoh_phi, as a wave-uniform branch.
 #pragma once
 
 #include "sscan_device.h"
@@ -195,7 +196,9 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
   // A past N: any nonzero value; that state's B row is zero, so it stays zero.
   const float Av = nlive ? Ag[drc * N + ln] : -1.f;
   const float rA = (Av != 0.f) ? 1.f / Av : 0.f;
-  const bool zeroA = __any(Av == 0.f);
+  // wave-uniform: some channel of the wave has a state with |A| small enough that the
+  // k-form's rounding error (of order ulp(x B / A) per step) would matter
+  const bool smallA = __any(fabsf(Av) < kSmallA);
 
   float h = 0.f;
   if (h_init && drvalid && nlive) h = h_init[((static_cast<int64_t>(seg) * sh.batch + b) * dim + dr) * N + ln];
@@ -354,7 +357,7 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
       ckpt_store(Par<Q>{}, c - 1);
     }
     float p[T];
-    if (EULER || !zeroA) {
+    if (EULER || !smallA) {
       static_for<0, T>([&](auto tc) {
         constexpr int t = decltype(tc)::value;
         if constexpr (t == 0 || t == 3 || t == 6) {
@@ -374,10 +377,11 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
         if constexpr (OUT) p[t] = cb[t >> 2][t & 3] * h;
       });
     } else {
-      // some A == 0 among the wave's channels: h <- Abar h + g B x with
-      // g = (Abar - 1)/A, or Delta where A == 0.  The broadcast is taken once, by
-      // every lane, and both candidates are formed before the select: a DPP read
-      // under a partial exec mask would see the inactive source lanes as zero.
+      // some small |A| (A == 0 included) among the wave's channels: the explicit
+      // update h <- Abar h + phi B x with the accurate phi = (Abar - 1)/A of zoh_phi.
+      // The broadcast is taken once, by every lane, and zoh_phi forms both of its
+      // candidates before its select: a DPP read under a partial exec mask would see
+      // the inactive source lanes as zero.
       read_bc(1);
       read_bc(2);
       read_bc(3);
@@ -385,9 +389,9 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
         constexpr int t = decltype(tc)::value;
         if constexpr (t % kBwdBlock == 0) checkpoint(pc, t / kBwdBlock);
         const float dl2 = row_bcast<t>(sd);
-        const float e = hw_exp2(dl2 * Av);
-        const float gz = (e - 1.f) * rA, g0 = dl2 * kLn2;
-        const float g = (Av != 0.f) ? gz : g0;
+        const float arg = dl2 * Av;
+        const float e = hw_exp2(arg);
+        const float g = zoh_phi(e, arg, dl2, rA);
         h = fmaf(e, h, g * (row_bcast<t>(sx) * bb[t >> 2][t & 3]));
         if constexpr (OUT) p[t] = cb[t >> 2][t & 3] * h;
       });

@@ -86,34 +86,47 @@ __global__ __launch_bounds__(256) void step_kernel(float* __restrict__ S, const 
 #pragma unroll
     for (int k = 0; k < SPL / 4; ++k) {
       if constexpr (VEC) {
-        const float4 hv = *reinterpret_cast<const float4*>(Sd + 4 * k);
-        const float4 av = *reinterpret_cast<const float4*>(Ad + 4 * k);
-        h[4 * k] = hv.x; h[4 * k + 1] = hv.y; h[4 * k + 2] = hv.z; h[4 * k + 3] = hv.w;
-        a[4 * k] = av.x; a[4 * k + 1] = av.y; a[4 * k + 2] = av.z; a[4 * k + 3] = av.w;
+        // N is a multiple of 4, so a group of 4 states lies wholly inside the row or
+        // wholly past it (N = 12: the second lane's upper group); a group past the row
+        // is neither read nor written, and contributes zero to C . h
+        if (NFIX > 0 || n0 + 4 * k < N) {
+          const float4 hv = *reinterpret_cast<const float4*>(Sd + 4 * k);
+          const float4 av = *reinterpret_cast<const float4*>(Ad + 4 * k);
+          h[4 * k] = hv.x; h[4 * k + 1] = hv.y; h[4 * k + 2] = hv.z; h[4 * k + 3] = hv.w;
+          a[4 * k] = av.x; a[4 * k + 1] = av.y; a[4 * k + 2] = av.z; a[4 * k + 3] = av.w;
+          load4<Tin, VEC>(Bp + b * N + n0 + 4 * k, n0 + 4 * k, N, bv + 4 * k);
+          load4<Tin, VEC>(Cp + b * N + n0 + 4 * k, n0 + 4 * k, N, cv + 4 * k);
+        } else {
+#pragma unroll
+          for (int j = 4 * k; j < 4 * k + 4; ++j) h[j] = a[j] = bv[j] = cv[j] = 0.f;
+        }
       } else {
 #pragma unroll
         for (int j = 4 * k; j < 4 * k + 4; ++j) {
           h[j] = (n0 + j < N) ? Sd[j] : 0.f;
           a[j] = (n0 + j < N) ? Ad[j] : 0.f;
         }
+        load4<Tin, VEC>(Bp + b * N + n0 + 4 * k, n0 + 4 * k, N, bv + 4 * k);
+        load4<Tin, VEC>(Cp + b * N + n0 + 4 * k, n0 + 4 * k, N, cv + 4 * k);
       }
-      load4<Tin, VEC>(Bp + b * N + n0 + 4 * k, n0 + 4 * k, N, bv + 4 * k);
-      load4<Tin, VEC>(Cp + b * N + n0 + 4 * k, n0 + 4 * k, N, cv + 4 * k);
     }
     const float d2 = softplus_log2e(v2);  // Delta * log2(e)
     const float dl = d2 * kLn2;           // Delta
 #pragma unroll
     for (int j = 0; j < SPL; ++j) {
-      const float e = hw_exp2(d2 * a[j]);
-      // (Abar - 1) / A, or Delta in the limit A = 0
-      const float g = (EULER || a[j] == 0.f) ? dl : (e - 1.f) * hw_rcp(a[j]);
+      const float arg = d2 * a[j];
+      const float e = hw_exp2(arg);
+      // (Abar - 1) / A, accurate for small |Delta A| (Delta in the limit A = 0); the
+      // step is bound by the state's memory traffic, so every channel takes this form
+      const float g = EULER ? dl : zoh_phi(e, arg, d2, a[j] != 0.f ? hw_rcp(a[j]) : 0.f);
       h[j] = fmaf(e, h[j], g * bv[j] * xv);
       yp = fmaf(cv[j], h[j], yp);
     }
 #pragma unroll
     for (int k = 0; k < SPL / 4; ++k) {
       if constexpr (VEC) {
-        *reinterpret_cast<float4*>(Sd + 4 * k) = make_float4(h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]);
+        if (NFIX > 0 || n0 + 4 * k < N)
+          *reinterpret_cast<float4*>(Sd + 4 * k) = make_float4(h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]);
       } else {
 #pragma unroll
         for (int j = 4 * k; j < 4 * k + 4; ++j)

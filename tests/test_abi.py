@@ -254,3 +254,34 @@ def test_bwd_checkpointed_validation(lib):
     assert bwd_ck(lib, ck=ctypes.c_void_p(0x80000)) == 1            # the checkpoints are dx
     assert b"overlap" in lib.sscan_last_error()
     assert bwd_ck(lib, N=17) == 2
+
+
+def test_seqlen_above_the_cap_is_invalid(lib):
+    # SSCAN_MAX_SEQLEN: the kernels count one segment's steps in 32-bit integers
+    cap = 1 << 30
+    text = open(HEADER).read()
+    assert re.search(r"#define SSCAN_MAX_SEQLEN \(1LL << 30\)", text)
+    assert fwd(lib, batch=1, L=cap + 1, dim=1, N=1) == 1
+    assert b"SSCAN_MAX_SEQLEN" in lib.sscan_last_error()
+    P = ctypes.c_void_p
+    # x, delta, A, B, C, D, z, bias, h0, dy, dlast, dx, ddelta, dA, dB, dC, dD, dz, dbias, dh0, workspace
+    args = [1, cap + 1, 1, 1, 0, 0, FAKE, FAKE2, P(0x30000), P(0x40000), P(0x50000), None, None, None, None,
+            P(0x60000), None, P(0x70000), P(0x80000), P(0x90000), P(0xA0000), P(0xC0000), None, None, None, None,
+            P(0xB0000), 1 << 20, None]
+    assert lib.sscan_bwd(*args) == 1
+
+
+@pytest.mark.parametrize("victim", ["x", "delta", "B", "C", "A", "initial_state", "last_state"])
+def test_split_workspace_overlapping_a_tensor_is_invalid(lib, victim):
+    # a forced 4-segment split writes its aggregates into the workspace before the main
+    # pass reads the inputs: a workspace over any tensor of the call is rejected before
+    # anything runs (the pointers below are never dereferenced)
+    P = ctypes.c_void_p
+    ptr = {"x": 0x100000, "delta": 0x200000, "A": 0x300000, "B": 0x400000, "C": 0x500000,
+           "initial_state": 0x600000, "last_state": 0x700000, "y": 0x800000}
+    ws = P(ptr[victim] + 16)
+    rc = lib.sscan_fwd_segmented(2, 256, 4, 4, 0, 0, P(ptr["x"]), P(ptr["delta"]), P(ptr["A"]), P(ptr["B"]),
+                                 P(ptr["C"]), None, None, None, P(ptr["initial_state"]), P(ptr["y"]),
+                                 P(ptr["last_state"]), ws, 1 << 16, 4, None)
+    assert rc == 1, lib.sscan_last_error()
+    assert b"workspace overlaps" in lib.sscan_last_error()

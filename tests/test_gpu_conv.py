@@ -74,15 +74,17 @@ def test_conv_fwd_mamba130m_layer(ss, orc):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_conv_prefill_then_decode(ss, orc, dtype):
+@pytest.mark.parametrize("N", [12, 16])
+def test_conv_prefill_then_decode(ss, orc, dtype, N):
     """Prefill k tokens with the fused forward, hand the scan state and the
     convolution cache to the decode step, step the rest: equals the oracle over the
-    whole sequence (page-3 report, sections 3 and 6)."""
+    whole sequence (page-3 report, sections 3 and 6).  N = 12: the decode step's
+    second lane of a row holds one group of 4 states and none past it."""
     import torch
-    w = W.make_scan_inputs(2, 40, 96, 16, dtype, seed=720, name="prefill + decode")
+    w = W.make_scan_inputs(2, 40, 96, N, dtype, seed=720, name="prefill + decode")
     K, k = 4, 29
     cw, cb, _ = conv_params(w.dim, K, 21, w.batch, with_state=False)
-    note(f"[case] conv prefill {k} + decode {w.seqlen - k} {dtype}")
+    note(f"[case] conv prefill {k} + decode {w.seqlen - k} {dtype} N={N}")
     sl = lambda a, lo, hi: None if a is None else np.ascontiguousarray(a[:, lo:hi])
     st = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device="cuda")
     cst = torch.empty((w.batch, w.dim, K - 1), dtype=torch.float32, device="cuda")

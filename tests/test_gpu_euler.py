@@ -51,7 +51,7 @@ def test_euler_differs_from_zoh(ss):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("N", [4, 7, 16])
+@pytest.mark.parametrize("N", [4, 7, 12, 16])
 def test_euler_step(ss, orc, dtype, N):
     import torch
     rng = np.random.default_rng(400 + N)

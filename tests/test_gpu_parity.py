@@ -316,7 +316,7 @@ def test_bf16_bc_two_byte_aligned(ss, orc, N):
 # single-token step
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("N", [1, 3, 4, 5, 8, 16])
+@pytest.mark.parametrize("N", [1, 3, 4, 5, 8, 12, 16])
 def test_step_small(ss, orc, dtype, N):
     import torch
     rng = np.random.default_rng(200 + N)
