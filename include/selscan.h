@@ -29,7 +29,8 @@
  *  - Arithmetic is float32 in registers (state included); y is rounded to
  *    `dtype` with round-to-nearest-even.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null
- *    stream).  The library allocates no device memory and never synchronizes.
+ *    stream).  The library allocates no device memory and never synchronizes
+ *    (sscan_fwd_noalloc's static scratch array comes with the loaded code object).
  *  - Errors: a nonzero sscan_status is returned and nothing is launched;
  *    sscan_last_error() gives a message (per calling thread).  Arguments are
  *    checked on the host before any launch.  Values are not checked: NaN and
@@ -133,6 +134,27 @@ int sscan_fwd_segmented(int64_t batch, int64_t seqlen, int64_t dim, int64_t dsta
                         const float* initial_state, void* y, float* last_state,
                         void* workspace, size_t workspace_bytes, int64_t num_segments,
                         void* stream);
+
+/*
+ * sscan_fwd for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Arguments, results
+ * and errors are those of sscan_fwd without the workspace; the two-level split's
+ * scratch (carries, segment end states, step sums) lives instead in a static device
+ * array of SSCAN_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs
+ * on until the process ends.  The call allocates nothing (no hipMalloc, no
+ * allocating library routine).  It chooses the same split as sscan_fwd with a
+ * workspace of sscan_fwd_workspace_size bytes, so its results equal that call's bit
+ * for bit; a shape whose split needs more scratch than the array holds is rejected
+ * with SSCAN_ERR_INVALID_ARG before anything runs.  Every call on one GPU shares
+ * that GPU's array: calls that overlap in time on one GPU (other streams, other
+ * threads) race on it and must be serialized by the caller.
+ */
+#define SSCAN_NOALLOC_SCRATCH_BYTES (32u << 20)
+int sscan_fwd_noalloc(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+                      unsigned int flags, const void* x, const void* delta, const float* A,
+                      const void* B, const void* C, const float* D, const void* z,
+                      const float* delta_bias, const float* initial_state, void* y,
+                      float* last_state, void* stream);
 
 /*
  * One recurrent step for a single token per batch row (decode).

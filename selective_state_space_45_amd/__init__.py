@@ -37,6 +37,8 @@ _lib.sscan_fwd.argtypes = [_I64, _I64, _I64, _I64, ctypes.c_int, _U32] + [_P] * 
 _lib.sscan_fwd.restype = ctypes.c_int
 _lib.sscan_fwd_segmented.argtypes = [_I64, _I64, _I64, _I64, ctypes.c_int, _U32] + [_P] * 11 + [_P, _SZ, _I64, _P]
 _lib.sscan_fwd_segmented.restype = ctypes.c_int
+_lib.sscan_fwd_noalloc.argtypes = [_I64, _I64, _I64, _I64, ctypes.c_int, _U32] + [_P] * 11 + [_P]
+_lib.sscan_fwd_noalloc.restype = ctypes.c_int
 _lib.sscan_step.argtypes = [_I64, _I64, _I64, ctypes.c_int, _U32] + [_P] * 11
 _lib.sscan_step.restype = ctypes.c_int
 _lib.sscan_fwd_conv.argtypes = [_I64, _I64, _I64, _I64, _I64, ctypes.c_int, _U32] + [_P] * 15 + [_P, _SZ, _P]
@@ -192,6 +194,42 @@ def sscan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Te
     if return_last_state:
         return y, ls
     return y
+
+
+def sscan_fwd_noalloc(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+                      D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+                      delta_bias: Optional[torch.Tensor] = None, initial_state: Optional[torch.Tensor] = None,
+                      out: Optional[torch.Tensor] = None, last_state: Optional[torch.Tensor] = None,
+                      euler: bool = False) -> torch.Tensor:
+    """``sscan_fwd`` for callers that cannot allocate: the library's static device
+    scratch replaces the workspace.  ``out`` (and ``last_state`` if wanted) must be
+    given, so this call allocates nothing either.  Returns ``out``."""
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, seqlen, dim]")
+    if out is None:
+        raise ValueError("out is required (the no-allocation path allocates nothing)")
+    batch, seqlen, dim = x.shape
+    if x.dtype not in _DTYPES:
+        raise ValueError("x must be float32 or bfloat16")
+    dstate = A.shape[1] if A.dim() == 2 else -1
+    _dev(x, "x")
+    _dev(delta, "delta", x.dtype, x.shape)
+    _dev(A, "A", torch.float32, (dim, dstate))
+    _dev(B, "B", x.dtype, (batch, seqlen, dstate))
+    _dev(C, "C", x.dtype, (batch, seqlen, dstate))
+    for t, name, shape in ((D, "D", (dim,)), (delta_bias, "delta_bias", (dim,)),
+                           (initial_state, "initial_state", (batch, dim, dstate)),
+                           (last_state, "last_state", (batch, dim, dstate))):
+        if t is not None:
+            _dev(t, name, torch.float32, shape)
+    if z is not None:
+        _dev(z, "z", x.dtype, x.shape)
+    _dev(out, "out", x.dtype, x.shape)
+    flags = SSCAN_FLAG_EULER if euler else 0
+    _check(_lib.sscan_fwd_noalloc(batch, seqlen, dim, dstate, _DTYPES[x.dtype], flags, _ptr(x), _ptr(delta),
+                                  _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                                  _ptr(initial_state), _ptr(out), _ptr(last_state), _stream(x.device)))
+    return out
 
 
 def sscan_step(state: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor,

@@ -177,6 +177,38 @@ int check_conv(const ConvArgs& cv, int64_t batch, int64_t dim) {
   return SSCAN_OK;
 }
 
+// Scratch of sscan_fwd_noalloc: the split forward's carries, segment end states and
+// step sums, in a static device array instead of a caller's workspace.  Each device
+// the library runs on holds one copy until the process ends.  In host code `scratch`
+// names a host-side stand-in, not device memory: kernels and copies get the address
+// that hipGetSymbolAddress reports for the current device (noalloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[SSCAN_NOALLOC_SCRATCH_BYTES];
+
+// Device address of `scratch` on the current device, looked up once per device (with
+// that device current) and cached; nullptr and an error message on failure.
+void* noalloc_scratch(int* rc) {
+  static std::mutex mu;
+  static std::vector<void*> ptrs;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0) {
+    *rc = hip_fail(e != hipSuccess ? e : hipErrorInvalidDevice, "hipGetDevice");
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lk(mu);
+  if (static_cast<int>(ptrs.size()) <= dev) ptrs.resize(dev + 1, nullptr);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      *rc = hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+      return nullptr;
+    }
+    ptrs[dev] = p;
+  }
+  return ptrs[dev];
+}
+
 int fwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype, unsigned flags, const void* x,
              const void* delta, const float* A, const void* B, const void* C, const float* D, const void* z,
              const float* delta_bias, const float* initial_state, void* y, float* last_state, void* workspace,
@@ -609,6 +641,28 @@ int sscan_fwd_conv(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, i
   return fwd_impl(batch, seqlen, dim, dstate, dtype, flags, x, delta, A, B, C, D, z, delta_bias, initial_state, y,
                   last_state, workspace, workspace_bytes, 0, stream,
                   ConvArgs{dconv, conv_w, conv_b, conv_state_in, conv_state_out});
+}
+
+int sscan_fwd_noalloc(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype, unsigned int flags,
+                      const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
+                      const void* z, const float* delta_bias, const float* initial_state, void* y,
+                      float* last_state, void* stream) {
+  // the split sscan_fwd would choose with an unlimited workspace; rejected if its
+  // scratch exceeds the static array (nothing is launched then)
+  const size_t need = sscan_fwd_workspace_size(batch, seqlen, dim, dstate, dtype);
+  if (need > SSCAN_NOALLOC_SCRATCH_BYTES)
+    return fail(SSCAN_ERR_INVALID_ARG,
+                "sscan_fwd_noalloc: this shape needs %zu bytes of scratch, above the static %zu "
+                "(SSCAN_NOALLOC_SCRATCH_BYTES); use sscan_fwd with a workspace",
+                need, static_cast<size_t>(SSCAN_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  if (need > 0) {
+    int rc = SSCAN_OK;
+    ws = noalloc_scratch(&rc);
+    if (!ws) return rc;
+  }
+  return fwd_impl(batch, seqlen, dim, dstate, dtype, flags, x, delta, A, B, C, D, z, delta_bias, initial_state, y,
+                  last_state, ws, ws ? static_cast<size_t>(SSCAN_NOALLOC_SCRATCH_BYTES) : 0, 0, stream, ConvArgs{});
 }
 
 int sscan_fwd_segmented(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,

@@ -285,3 +285,17 @@ def test_split_workspace_overlapping_a_tensor_is_invalid(lib, victim):
                                  P(ptr["last_state"]), ws, 1 << 16, 4, None)
     assert rc == 1, lib.sscan_last_error()
     assert b"workspace overlaps" in lib.sscan_last_error()
+
+
+def test_noalloc_rejects_scratch_above_the_maximum(lib):
+    # the rejection happens on the host, before the static scratch is looked up
+    P, I64 = ctypes.c_void_p, ctypes.c_int64
+    lib.sscan_fwd_noalloc.argtypes = [I64, I64, I64, I64, ctypes.c_int, ctypes.c_uint] + [P] * 11 + [P]
+    text = open(HEADER).read()
+    assert re.search(r"#define SSCAN_NOALLOC_SCRATCH_BYTES \(32u << 20\)", text)
+    need = lib.sscan_fwd_workspace_size(6, 65536, 1536, 16, 1)
+    assert need > (32 << 20)
+    rc = lib.sscan_fwd_noalloc(6, 65536, 1536, 16, 1, 0, FAKE, FAKE2, P(0x30000), P(0x40000), P(0x50000),
+                               None, None, None, None, P(0x60000), None, None)
+    assert rc == 1
+    assert b"SSCAN_NOALLOC_SCRATCH_BYTES" in lib.sscan_last_error()
