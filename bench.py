@@ -28,12 +28,19 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0                       # MI355X HBM3E
+FLUSH_BYTES = 1 << 30                        # cache flush between timed launches (L2 + 256 MB MALL)
+DECODE_STATES = 5                            # decode states cycled per graph (5 x 84 MB > MALL)
 # VALU issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz fp32 lane-operations per second
 # (packed FP32 disabled in this build, so one fp32 op per lane per cycle).
 PEAK_VALU_TOPS = 256 * 64 * 2.4e9 / 1e12
 # Algorithmic VALU operations (an exp/log/rcp counts 2: half-rate on CDNA4):
 OPS_PER_STATE_UPDATE = 8     # Delta*A, exp (2), B/A scale, x scale, add, fma (state), fma (readout)
 OPS_PER_TOKEN_CHANNEL = 20   # softplus 11, silu 7, skip + gate 2
+# Backward pass, per (b, l, d, n): checkpoint-pass recurrence 8, recompute 9, reverse step
+# with its gradient terms 20, sums over lanes 4 (about 42 with the exp counted 2); per
+# (b, l, d): softplus and its derivative, silu and its derivative, skip and gate ~40.
+OPS_PER_STATE_UPDATE_BWD = 41
+OPS_PER_TOKEN_CHANNEL_BWD = 40
 PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "sscan_fwd_train_shape_counters.json")
 COPY_ELEMS = 128 << 20                       # calibration copy: 512 MiB of fp32
 KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_45_amd", "csrc", f)
@@ -122,7 +129,7 @@ def summarize_counters(fetch_csv: str, write_csv: str) -> dict:
 
 def per_config_report() -> None:
     """One JSON line per workload (documentation mode, --configs): GPU time (median of
-    HIP-event-timed launches, inputs resident), effective GB/s, the oracle's time on the
+    50 HIP-event-timed launches, inputs resident, L2 and MALL flushed before each), effective GB/s, the oracle's time on the
     host cores, and the max error against the oracle under the parity-test metric."""
     import numpy as np
     import torch
@@ -138,19 +145,14 @@ def per_config_report() -> None:
         t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
         return t.to(torch.bfloat16) if dtype == "bf16" else t
 
-    def median_ms(fn, n=20, warm=3):
+    flush = Flush(torch, dev)
+
+    def median_ms(fn, n=50, warm=3):
+        # median of n launches, each after a write that evicts L2 and the MALL
         for _ in range(warm):
             fn()
         torch.cuda.synchronize()
-        ts = []
-        for _ in range(n):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            fn()
-            e1.record()
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        return float(np.median(ts))
+        return timed_median(torch, fn, n, flush)[0]
 
     for name in ("tiny", "mamba130m_layer", "train_shape", "long_context"):
         w = W.workload(name)
@@ -214,7 +216,7 @@ def per_config_report() -> None:
     with torch.cuda.graph(g):
         for _ in range(20):
             ss.sscan_step(sd, tx, tdt, dA, tB, tC, D=dD, z=tz, out=yd)
-    ms = median_ms(g.replay) / 20
+    ms = median_ms(g.replay, n=20) / 20
     st_ref = dw.state0.astype(np.float64)
     t0 = time.perf_counter()
     oracle.sscan_step(st_ref, tk.x, tk.dt, dw.A, tk.B, tk.C, D=dw.D, z=tk.z)
@@ -225,6 +227,56 @@ def per_config_report() -> None:
                       "hbm_frac": round(nb / (ms * 1e-3) / 1e9 / 8000, 4), "oracle_s_per_step": round(cpu_s, 4),
                       "oracle_threads": oracle.last_threads_used(),
                       "note": "errors over 1000 steps are checked by the parity tests"}), flush=True)
+
+
+class Flush:
+    """Evicts the L2 caches and the 256 MB MALL between timed launches by writing a
+    1 GiB buffer (a fill kernel on the timing stream, outside the timed events)."""
+
+    def __init__(self, torch, dev, nbytes=FLUSH_BYTES):
+        self.buf = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
+
+    def __call__(self):
+        self.buf.fill_(1.0)
+
+
+def timed_median(torch, fn, n, flush=None):
+    """Median (and mean) of n launches of fn timed by HIP events on torch's current
+    stream (the stream the library launches on), each after a cache flush."""
+    import numpy as np
+    ts = []
+    for _ in range(n):
+        if flush is not None:
+            flush()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return float(np.median(ts)), float(np.mean(ts))
+
+
+def roofline_entry(nbytes, ops, kern_ms, kernel, timing):
+    """Roofline of the dominant kernel against the metric's peak (HBM), with the vector
+    ALU issue fraction beside it.  'bound' names the resource whose time at its peak is
+    the larger for the algorithmic work of one launch (bytes at 8 TB/s against VALU
+    lane-operations at the non-packed issue rate)."""
+    gbs = nbytes / (kern_ms * 1e-3) / 1e9
+    tops = ops / (kern_ms * 1e-3) / 1e12
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    t_alu = ops / (PEAK_VALU_TOPS * 1e12)
+    return {"bound": "alu" if t_alu > t_hbm else "hbm",
+            "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "traffic": measured_traffic(),
+            "kernel": kernel, "kernel_ms": round(kern_ms, 5), "timing": timing,
+            "algorithmic_bytes": nbytes,
+            "alu": {"achieved": round(tops, 3), "peak": round(PEAK_VALU_TOPS, 3), "unit": "T lane-op/s",
+                    "frac": round(tops / PEAK_VALU_TOPS, 4), "algorithmic_ops": ops,
+                    "peak_derivation": "256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz: the published 157.3 TFLOP/s fp32 "
+                                       "/ 2 (an FMA counts 2 flops) / 2 (packed FP32, not used)",
+                    "time_at_peak_us": round(t_alu * 1e6, 1)},
+            "hbm_time_at_peak_us": round(t_hbm * 1e6, 1)}
 
 
 def main():
@@ -248,6 +300,8 @@ def main():
     ap.add_argument("--no-conv", action="store_true", help="skip the convolution-prologue leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 512 MiB elementwise copy (counter calibration)")
+    ap.add_argument("--kernel-runs", type=int, default=60,
+                    help="flushed, individually timed launches behind roofline.kernel_ms (median)")
     ap.add_argument("--decode-steps", type=int, default=100)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -272,53 +326,46 @@ def main():
     st = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev)
     wsb = ss.fwd_workspace_size(w.batch, w.seqlen, w.dim, w.dstate, torch.bfloat16)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    flush = Flush(torch, dev)
 
     def step():
         ss.sscan_fwd(x, dt, A, B, C, D=D, z=z, delta_bias=bias, out=y, last_state=st, workspace=ws)
 
+    # the timed region: K back-to-back steps, inputs resident in HBM
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # per-launch HIP events on the stream the kernels run on (torch's current stream)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for e0, e1 in evs:
-        e0.record()
+    for _ in range(args.steps):
         step()
-        e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    launch_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
     ms_per_step = wall * 1e3 / args.steps
-    kern_ms = float(np.mean(launch_ms))
 
     nbytes = W.fwd_algorithmic_bytes(w.batch, w.seqlen, w.dim, w.dstate, "bf16")
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     tokch = w.batch * w.seqlen * w.dim
     ops = tokch * w.dstate * OPS_PER_STATE_UPDATE + tokch * OPS_PER_TOKEN_CHANNEL
-    achieved_tops = ops / (kern_ms * 1e-3) / 1e12
-    kern_gbs = nbytes / (kern_ms * 1e-3) / 1e9
 
-    # the Euler rule (Bbar = Delta B) on the same workload, reported alongside
-    def timed_launches(fn, n):
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-        for e0, e1 in ev:
-            e0.record()
+    # the dominant kernel on its own: median of flushed launches (one sscan_fwd call is
+    # one kernel launch on this shape)
+    nruns = max(50, args.kernel_runs)
+    kern_ms, kern_mean = timed_median(torch, step, nruns, flush)
+    roof = roofline_entry(nbytes, ops, kern_ms, "fwd_row_kernel<bf16, output mode, N=16, zero-order hold>",
+                          f"median of {nruns} launches, HIP events on the launch stream, each after a "
+                          f"{FLUSH_BYTES >> 20} MiB write that evicts L2 and MALL")
+    roof["kernel_ms_mean"] = round(kern_mean, 5)
+
+    def leg_ms(fn, n):
+        for _ in range(3):
             fn()
-            e1.record()
         torch.cuda.synchronize()
-        return float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
-
-    def step_euler():
-        ss.sscan_fwd(x, dt, A, B, C, D=D, z=z, delta_bias=bias, out=y, last_state=st, workspace=ws, euler=True)
+        return timed_median(torch, fn, n, flush)[0]
 
     euler = None
     if not args.no_euler:
-        for _ in range(3):
-            step_euler()
-        torch.cuda.synchronize()
-        eu_ms = timed_launches(step_euler, max(5, args.steps // 2))
+        eu_ms = leg_ms(lambda: ss.sscan_fwd(x, dt, A, B, C, D=D, z=z, delta_bias=bias, out=y, last_state=st,
+                                            workspace=ws, euler=True), max(10, args.steps // 2))
         euler = {"op": "sscan_fwd, Euler rule (flag SSCAN_FLAG_EULER)", "kernel_ms": round(eu_ms, 5),
                  "gbs": round(nbytes / (eu_ms * 1e-3) / 1e9, 2),
                  "hbm_frac_of_peak": round(nbytes / (eu_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
@@ -332,15 +379,9 @@ def main():
         cb = torch.randn(w.dim, device=dev) * 0.1
         cs_in = torch.randn(w.batch, w.dim, K - 1, device=dev)
         cs_out = torch.empty_like(cs_in)
-
-        def step_conv():
-            ss.sscan_fwd(x, dt, A, B, C, D=D, z=z, delta_bias=bias, out=y, last_state=st, workspace=ws,
-                         conv_w=cw, conv_b=cb, conv_state_in=cs_in, conv_state_out=cs_out)
-
-        for _ in range(3):
-            step_conv()
-        torch.cuda.synchronize()
-        cv_ms = timed_launches(step_conv, max(5, args.steps // 2))
+        cv_ms = leg_ms(lambda: ss.sscan_fwd(x, dt, A, B, C, D=D, z=z, delta_bias=bias, out=y, last_state=st,
+                                            workspace=ws, conv_w=cw, conv_b=cb, conv_state_in=cs_in,
+                                            conv_state_out=cs_out), max(10, args.steps // 2))
         cv_bytes = nbytes + 4 * w.dim * (K + 1) + 2 * 4 * w.batch * w.dim * (K - 1)
         conv = {"op": "sscan_fwd_conv (fused causal conv1d, 4 taps, + SiLU prologue)", "ms": round(cv_ms, 5),
                 "algorithmic_bytes": cv_bytes, "gbs": round(cv_bytes / (cv_ms * 1e-3) / 1e9, 2)}
@@ -353,18 +394,16 @@ def main():
         bwd_ws = torch.empty(ss.bwd_workspace_size(w.batch, w.seqlen, w.dim, w.dstate, torch.bfloat16),
                              dtype=torch.uint8, device=dev)
         grads = {}
-
-        def step_bwd():
-            ss.sscan_bwd(x, dt, A, B, C, gy, D=D, z=z, delta_bias=bias, workspace=bwd_ws, out=grads)
-
-        for _ in range(3):
-            step_bwd()
-        torch.cuda.synchronize()
-        bw_ms = timed_launches(step_bwd, max(5, args.steps // 5))
-        # inputs x, dt, z, dy, B, C (+A, D, bias) read once; dx, ddt, dz, dB, dC (+dA, dD, dbias) written once
+        bw_ms = leg_ms(lambda: ss.sscan_bwd(x, dt, A, B, C, gy, D=D, z=z, delta_bias=bias, workspace=bwd_ws,
+                                            out=grads), max(10, args.steps // 5))
         bw_bytes = W.bwd_algorithmic_bytes(w.batch, w.seqlen, w.dim, w.dstate, "bf16")
+        bw_ops = tokch * w.dstate * OPS_PER_STATE_UPDATE_BWD + tokch * OPS_PER_TOKEN_CHANNEL_BWD
         bwd = {"op": "sscan_bwd (checkpoint pass + reverse pass + reductions)", "ms": round(bw_ms, 5),
                "algorithmic_bytes": bw_bytes, "gbs": round(bw_bytes / (bw_ms * 1e-3) / 1e9, 2),
+               "hbm_frac_of_peak": round(bw_bytes / (bw_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+               "alu": {"algorithmic_ops": bw_ops, "achieved": round(bw_ops / (bw_ms * 1e-3) / 1e12, 3),
+                       "peak": round(PEAK_VALU_TOPS, 3), "unit": "T lane-op/s",
+                       "frac": round(bw_ops / (bw_ms * 1e-3) / 1e12 / PEAK_VALU_TOPS, 4)},
                "tokens_channels_per_s": round(tokch / (bw_ms * 1e-3), 1)}
 
         # a training step's scan: the forward saves the state every 8 steps and the
@@ -375,43 +414,37 @@ def main():
                                                   checkpointed=True), dtype=torch.uint8, device=dev)
         y_t = torch.empty_like(x)
         st_t = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev)
-
-        def step_fwd_ck():
-            ss.sscan_fwd(x, dt, A, B, C, D=D, z=z, delta_bias=bias, out=y_t, last_state=st_t, checkpoints=ck)
-
-        def step_bwd_ck():
-            ss.sscan_bwd(x, dt, A, B, C, gy, D=D, z=z, delta_bias=bias, workspace=ck_ws, out=grads, checkpoints=ck)
-
-        for _ in range(3):
-            step_fwd_ck()
-            step_bwd_ck()
-        torch.cuda.synchronize()
-        fck_ms = timed_launches(step_fwd_ck, max(5, args.steps // 5))
-        bck_ms = timed_launches(step_bwd_ck, max(5, args.steps // 5))
+        fck_ms = leg_ms(lambda: ss.sscan_fwd(x, dt, A, B, C, D=D, z=z, delta_bias=bias, out=y_t, last_state=st_t,
+                                             checkpoints=ck), max(10, args.steps // 5))
+        bck_ms = leg_ms(lambda: ss.sscan_bwd(x, dt, A, B, C, gy, D=D, z=z, delta_bias=bias, workspace=ck_ws,
+                                             out=grads, checkpoints=ck), max(10, args.steps // 5))
         bwd["train_step"] = {
             "op": "sscan_fwd with checkpoints, then sscan_bwd from them (no recompute pass)",
             "fwd_ms": round(fck_ms, 5), "bwd_ms": round(bck_ms, 5), "ms": round(fck_ms + bck_ms, 5),
-            "vs_fwd_plus_bwd_ms": round(ms_per_step + bw_ms, 5)}
+            "vs_fwd_plus_bwd_ms": round(kern_ms + bw_ms, 5)}
+        del gy, bwd_ws, grads, ck, ck_ws, y_t, st_t
 
     # decode step (sscan_step) on the decode workload, reported alongside.  The steps
     # are captured in a HIP graph and replayed, so host-side launch overhead is not
-    # counted (the kernel needs ~25 us, about what one Python-side launch costs).
+    # counted.  They cycle over several state buffers (each its own sequence of tokens'
+    # state) whose total exceeds the 256 MB MALL, so each step reads its state from HBM.
     decode = None
     if not args.no_decode:
         dw = W.DecodeWorkload()
         tk = dw.token(0)
-        sd = f32(dw.state0)
+        nstates = DECODE_STATES
+        states = [f32(dw.state0) for _ in range(nstates)]
         tx, tdt, tz, tB, tC = bf(tk.x), bf(tk.dt), bf(tk.z), bf(tk.B), bf(tk.C)
         dA, dD = f32(dw.A), f32(dw.D)
         yd = torch.empty_like(tx)
-        for _ in range(3):
+        for sd in states:
             ss.sscan_step(sd, tx, tdt, dA, tB, tC, D=dD, z=tz, out=yd)
         torch.cuda.synchronize()
-        per_graph = 20
+        per_graph = 4 * nstates
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for _ in range(per_graph):
-                ss.sscan_step(sd, tx, tdt, dA, tB, tC, D=dD, z=tz, out=yd)
+            for i in range(per_graph):
+                ss.sscan_step(states[i % nstates], tx, tdt, dA, tB, tC, D=dD, z=tz, out=yd)
         g.replay()
         torch.cuda.synchronize()
         reps = max(1, args.decode_steps // per_graph)
@@ -426,7 +459,10 @@ def main():
         decode = {"op": "sscan_step", "workload": "batch 256, dim 5120, dstate 16, bf16 token, fp32 state",
                   "us_per_step": round(dec_ms * 1e3, 2), "gbs": round(dec_bytes / (dec_ms * 1e-3) / 1e9, 2),
                   "hbm_frac_of_peak": round(dec_bytes / (dec_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                  "timing": f"HIP graph of {per_graph} steps replayed {reps} times"}
+                  "timing": f"HIP graph of {per_graph} steps cycling over {nstates} states "
+                            f"({nstates * dw.batch * dw.dim * dw.dstate * 4 / 1e6:.0f} MB, above the 256 MB MALL), "
+                            f"replayed {reps} times"}
+        del states, g
 
     if args.copy_calibration:
         src = torch.ones(COPY_ELEMS, dtype=torch.float32, device=dev)
@@ -447,12 +483,22 @@ def main():
                              dt_bias=w.dt_bias)
             cpu_s += time.perf_counter() - t0
             reps += 1
+        threads = oracle.last_threads_used()
         sample_bytes = reps * W.fwd_algorithmic_bytes(rows, w.seqlen, w.dim, w.dstate, "bf16")
-        cpu = {"value": round(sample_bytes / cpu_s / 1e9, 4), "unit": "GB/s", "cores": oracle.last_threads_used(),
-               "kind": "oracle",
+        # one thread on one batch row (1/8 of the workload), extrapolated to the whole
+        t0 = time.perf_counter()
+        oracle.sscan_fwd(w.x[:1], w.dt[:1], w.A, w.B[:1], w.C[:1], D=w.D, z=w.z[:1], dt_bias=w.dt_bias, nthreads=1)
+        one_s = time.perf_counter() - t0
+        one_bytes = W.fwd_algorithmic_bytes(1, w.seqlen, w.dim, w.dstate, "bf16")
+        cpu = {"value": round(sample_bytes / cpu_s / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
                "sample": f"the whole training-shape workload (batch {rows}, L=4096, D=2048, N=16) {reps} times, "
-                         f"fp64 sequential recurrence, {cpu_s:.2f} s wall",
-               "tokens_channels_per_s": round(reps * rows * w.seqlen * w.dim / cpu_s, 1)}
+                         f"fp64 sequential recurrence, {cpu_s:.2f} s wall on {threads} threads",
+               "tokens_channels_per_s": round(reps * rows * w.seqlen * w.dim / cpu_s, 1),
+               "one_thread": {"value": round(one_bytes / one_s / 1e9, 5), "unit": "GB/s",
+                              "whole_workload_s_extrapolated": round(one_s * w.batch, 2),
+                              "sample": f"one batch row (1/{w.batch} of the workload) on 1 thread: {one_s:.2f} s; "
+                                        f"the whole-workload time is that times {w.batch} (extrapolated, "
+                                        "not measured)"}}
 
     out = {
         "metric": "selective-scan fwd GB/s effective + % of HBM peak (B=8,L=4096,D=2048,N=16)",
@@ -473,12 +519,7 @@ def main():
                    "io_dtype": "bf16", "state_dtype": "f32", "segments": 1 if wsb == 0 else "auto"},
         "hbm_frac_of_peak": round(value / PEAK_HBM_GBS, 4),
         "tokens_channels_per_s": round(tokch / (ms_per_step * 1e-3), 1),
-        "roofline": {"bound": "alu", "achieved": round(achieved_tops, 3), "peak": round(PEAK_VALU_TOPS, 3),
-                     "unit": "Top/s", "frac": round(achieved_tops / PEAK_VALU_TOPS, 4),
-                     "traffic": measured_traffic(),
-                     "kernel": "fwd_row_kernel<bf16, output mode, N=16, zero-order hold>",
-                     "kernel_ms": round(kern_ms, 5), "kernel_gbs": round(kern_gbs, 2),
-                     "algorithmic_bytes": nbytes, "algorithmic_ops": ops},
+        "roofline": roof,
         "euler": euler,
         "conv": conv,
         "bwd": bwd,

@@ -34,20 +34,49 @@ def _run(cmd, verbose):
     return res.returncode, msgs
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source to an object (in parallel), then link libselscan.so."""
+def _source_key(src: str) -> str:
+    """Hash of one translation unit's inputs: its source, every header it can include
+    (all of csrc/*.h and the public header) and the compiler flags."""
+    import glob
+    import hashlib
+    h = hashlib.sha256(" ".join(HIPCC_FLAGS).encode())
+    for f in [os.path.join(HERE, src)] + sorted(glob.glob(os.path.join(HERE, "csrc", "*.h"))) + \
+            [os.path.join(ROOT, "include", "selscan.h")]:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def build(verbose: bool = False, incremental: bool = False) -> str:
+    """Compile every source to an object (in parallel), then link libselscan.so.
+
+    incremental: keep objects in _build/ keyed by a hash of their inputs and reuse
+    those that are current (a development convenience; the default compiles all)."""
     from concurrent.futures import ThreadPoolExecutor
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
     tag = "%d" % os.getpid()
-    objs = [os.path.join(objdir, os.path.basename(src).replace(".hip", ".%s.o" % tag)) for src in SOURCES]
+    if incremental:
+        objs = [os.path.join(objdir, os.path.basename(src).replace(".hip", ".%s.o" % _source_key(src)))
+                for src in SOURCES]
+    else:
+        objs = [os.path.join(objdir, os.path.basename(src).replace(".hip", ".%s.o" % tag)) for src in SOURCES]
     compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
-    jobs = [[hipcc()] + compile_flags + ["-I" + os.path.join(ROOT, "include"), "-c", "-o", o,
-                                         os.path.join(HERE, src)] for src, o in zip(SOURCES, objs)]
+    jobs = [(src, o, [hipcc()] + compile_flags + ["-I" + os.path.join(ROOT, "include"), "-c", "-o", o + ".tmp" + tag,
+                                                  os.path.join(HERE, src)])
+            for src, o in zip(SOURCES, objs) if not (incremental and os.path.exists(o))]
+
+    def compile_one(job):
+        src, o, cmd = job
+        rc, msgs = _run(cmd, verbose)
+        if rc == 0:
+            os.replace(o + ".tmp" + tag, o)
+        return rc, msgs, src
+
     try:
-        with ThreadPoolExecutor(max(1, min(len(jobs), os.cpu_count() or 1))) as ex:
-            results = list(ex.map(lambda c: _run(c, verbose), jobs))
-        for (rc, msgs), src in zip(results, SOURCES):
+        with ThreadPoolExecutor(max(1, min(len(jobs) or 1, os.cpu_count() or 1))) as ex:
+            results = list(ex.map(compile_one, jobs))
+        for rc, msgs, src in results:
             if rc != 0:
                 sys.stderr.write("\n".join(msgs) + "\n")
                 raise RuntimeError("hipcc failed compiling %s" % src)
@@ -60,11 +89,12 @@ def build(verbose: bool = False) -> str:
             raise RuntimeError("hipcc failed linking libselscan.so")
         os.replace(tmp, LIB)
     finally:
-        for o in objs:
-            if os.path.exists(o):
-                os.remove(o)
+        if not incremental:
+            for o in objs:
+                if os.path.exists(o):
+                    os.remove(o)
     return LIB
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, incremental="--incremental" in sys.argv))
