@@ -7,7 +7,7 @@ bf16 x/delta/z/B/C/y, fp32 A/D/bias/state.  Inputs are resident in HBM before th
 timed region.  One JSON line is printed.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
-                    [--no-euler] [--no-bwd] [--no-conv] [--copy-calibration]
+                    [--no-euler] [--no-structured] [--no-bwd] [--no-conv] [--copy-calibration]
     python bench.py --summarize-counters FETCH_CSV WRITE_CSV   (CPU only)
     python bench.py --configs     (one line per workload: GPU time, GB/s, oracle time, error)
 
@@ -296,6 +296,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline leg")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step leg")
     ap.add_argument("--no-euler", action="store_true", help="skip the Euler-rule leg")
+    ap.add_argument("--no-structured", action="store_true", help="skip the structured-A leg")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward-pass leg")
     ap.add_argument("--no-conv", action="store_true", help="skip the convolution-prologue leg")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -361,6 +362,19 @@ def main():
             fn()
         torch.cuda.synchronize()
         return timed_median(torch, fn, n, flush)[0]
+
+    # the structured-A path (SSCAN_FLAG_STRUCTURED_A) on the same workload, whose
+    # A = -(n + 1) is rank one: reported beside the general path, never as the headline
+    structured = None
+    if not args.no_structured:
+        sa_ms = leg_ms(lambda: ss.sscan_fwd(x, dt, A, B, C, D=D, z=z, delta_bias=bias, out=y, last_state=st,
+                                            workspace=ws, structured_a=True), nruns)
+        structured = {"op": "sscan_fwd with SSCAN_FLAG_STRUCTURED_A (x / c_d and B / a_n staged; A = -(n+1) "
+                            "verified rank one per channel tile)",
+                      "kernel": "fwd_row_kernel<bf16, output mode, N=16, zero-order hold, factored A>",
+                      "kernel_ms": round(sa_ms, 5), "gbs": round(nbytes / (sa_ms * 1e-3) / 1e9, 2),
+                      "hbm_frac_of_peak": round(nbytes / (sa_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                      "vs_general_kernel": round(kern_ms / sa_ms, 4)}
 
     euler = None
     if not args.no_euler:
@@ -520,6 +534,7 @@ def main():
         "hbm_frac_of_peak": round(value / PEAK_HBM_GBS, 4),
         "tokens_channels_per_s": round(tokch / (ms_per_step * 1e-3), 1),
         "roofline": roof,
+        "structured_a": structured,
         "euler": euler,
         "conv": conv,
         "bwd": bwd,

@@ -69,6 +69,21 @@ extern "C" {
  */
 #define SSCAN_FLAG_EULER 1u
 
+/*
+ * SSCAN_FLAG_STRUCTURED_A: the caller states that A is rank one, A[d, n] = c_d a_n --
+ *   as the S4D-Real initialisation A = -(n + 1) of every channel (Mamba_Model_Report.md,
+ *   section 3, MambaBlock: A = -exp(A_log) with A_log = log(1 .. N) for each channel).
+ *   Then x B / A = (x / c_d)(B / a_n), and the forward stages x / c_d and B / a_n once
+ *   per token instead of dividing per state.  A hint, never a change of the result:
+ *   each channel tile checks the form exactly (c_d = A[d, 0], a_n = A[d0, n] / A[d0, 0]
+ *   for the tile's first channel d0, and c_d a_n == A[d, n] with no rounding) and runs
+ *   the plain form where it does not hold; results agree with the flag's absence to
+ *   float32 rounding.  Used by sscan_fwd, sscan_fwd_segmented and sscan_fwd_noalloc with
+ *   the zero-order hold when the launch takes the row layout (grids of at most one
+ *   workgroup per compute unit); ignored otherwise and by the other entry points.
+ */
+#define SSCAN_FLAG_STRUCTURED_A 2u
+
 typedef enum {
   SSCAN_OK = 0,
   SSCAN_ERR_INVALID_ARG = 1,  /* bad size, null required pointer, overlap, misalignment */

@@ -61,6 +61,7 @@ _lib.sscan_bwd_checkpointed.restype = ctypes.c_int
 
 SSCAN_F32, SSCAN_BF16 = 0, 1
 SSCAN_FLAG_EULER = 1
+SSCAN_FLAG_STRUCTURED_A = 2
 _DTYPES = {torch.float32: SSCAN_F32, torch.bfloat16: SSCAN_BF16}
 STATUS = {0: "SSCAN_OK", 1: "SSCAN_ERR_INVALID_ARG", 2: "SSCAN_ERR_UNSUPPORTED", 3: "SSCAN_ERR_HIP"}
 
@@ -121,7 +122,7 @@ def sscan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Te
               num_segments: Optional[int] = None, euler: bool = False,
               conv_w: Optional[torch.Tensor] = None, conv_b: Optional[torch.Tensor] = None,
               conv_state_in: Optional[torch.Tensor] = None, conv_state_out: Optional[torch.Tensor] = None,
-              checkpoints: Optional[torch.Tensor] = None):
+              checkpoints: Optional[torch.Tensor] = None, structured_a: bool = False):
     """Forward selective scan.  x, delta, z: [batch, seqlen, dim]; B, C: [batch, seqlen, dstate]
     (all float32 or all bfloat16); A: [dim, dstate], D, delta_bias: [dim], initial_state:
     [batch, dim, dstate] (float32).  euler: Bbar = Delta B instead of the zero-order hold.
@@ -129,7 +130,8 @@ def sscan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Te
     convolution + SiLU prologue (conv_b [dim], conv_state_in / conv_state_out
     [batch, dim, dconv - 1], float32, optional).  checkpoints (a device buffer of at least
     ``checkpoint_bytes(...)`` bytes): also save the states that ``sscan_bwd(...,
-    checkpoints=...)`` starts from.  Returns y, or (y, last_state)."""
+    checkpoints=...)`` starts from.  structured_a: the caller states A[d, n] = c_d a_n
+    (SSCAN_FLAG_STRUCTURED_A, a hint the library verifies).  Returns y, or (y, last_state)."""
     if x.dim() != 3:
         raise ValueError("x must be [batch, seqlen, dim]")
     batch, seqlen, dim = x.shape
@@ -163,7 +165,7 @@ def sscan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Te
             need = max(need, 4 * num_segments * batch * dim * (2 * dstate + 1))
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device) if need > 0 else None
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    flags = SSCAN_FLAG_EULER if euler else 0
+    flags = (SSCAN_FLAG_EULER if euler else 0) | (SSCAN_FLAG_STRUCTURED_A if structured_a else 0)
     args = [batch, seqlen, dim, dstate, dt, flags, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
             _ptr(delta_bias), _ptr(initial_state), _ptr(y), _ptr(ls), _ptr(workspace), wbytes]
     if conv_w is not None:

@@ -147,7 +147,8 @@ struct Buf {
 
 int check_common(int64_t batch, int64_t dim, int64_t dstate, int dtype, unsigned flags) {
   if (dtype != SSCAN_F32 && dtype != SSCAN_BF16) return fail(SSCAN_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
-  if (flags & ~SSCAN_FLAG_EULER) return fail(SSCAN_ERR_UNSUPPORTED, "unknown flag bits 0x%x", flags);
+  if (flags & ~(SSCAN_FLAG_EULER | SSCAN_FLAG_STRUCTURED_A))
+    return fail(SSCAN_ERR_UNSUPPORTED, "unknown flag bits 0x%x", flags);
   if (dstate < 1 || dstate > SSCAN_MAX_DSTATE)
     return fail(SSCAN_ERR_UNSUPPORTED, "dstate %lld outside [1, %d]", (long long)dstate, SSCAN_MAX_DSTATE);
   if (batch < 0 || dim < 0) return fail(SSCAN_ERR_INVALID_ARG, "negative size (batch %lld, dim %lld)",
@@ -315,6 +316,7 @@ int fwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dty
   p.seg_len = pl.seg_len; p.nseg = pl.nseg;
   p.npw = fwd_states_per_wave(N, p.ndtiles * batch * pl.nseg);
   p.euler = (flags & SSCAN_FLAG_EULER) != 0;
+  p.structured = (flags & SSCAN_FLAG_STRUCTURED_A) != 0;
   p.conv_w = cv.w; p.conv_b = cv.b; p.conv_s = cv.state_in; p.dconv = static_cast<int>(cv.w ? cv.dconv : 0);
   p.ckpt = ckpt_out; p.nblk = nblk;
   const bool bf16 = dtype == SSCAN_BF16;

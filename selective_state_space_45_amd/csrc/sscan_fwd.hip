@@ -25,6 +25,7 @@ extern template hipError_t launch_fwd_row<kFwdCkpt, true>(const FwdParams&, bool
 extern template hipError_t launch_fwd_row<kFwdOutCkpt, true>(const FwdParams&, bool, hipStream_t);
 extern template hipError_t launch_fwd_row<kFwdOutConv, false>(const FwdParams&, bool, hipStream_t);
 extern template hipError_t launch_fwd_row<kFwdOutConv, true>(const FwdParams&, bool, hipStream_t);
+extern template hipError_t launch_fwd_row<kFwdOut, false, true>(const FwdParams&, bool, hipStream_t);
 
 // carry[s] = state entering segment s: carry[0] = h_init (or 0),
 // carry[s+1] = exp2(A * S_s) * carry[s] + hend_s, where S_s is the segment's sum of
@@ -85,6 +86,11 @@ hipError_t launch_fwd_mode(const FwdParams& p, bool bf16, hipStream_t s) {
       return p.euler ? launch_fwd_variant<MODE, true, true>(p, bf16, s)
                      : launch_fwd_variant<MODE, false, true>(p, bf16, s);
     }
+  }
+  if constexpr (MODE == kFwdOut) {
+    // a rank-one A stated by the caller: the row layout's factored staging (it checks
+    // the form per workgroup and falls back to the plain staging where it fails)
+    if (p.structured && !p.euler && fwd_row_layout(p)) return launch_fwd_row<kFwdOut, false, true>(p, bf16, s);
   }
   if constexpr (MODE != kFwdAgg) {
     // the checkpoint pass always runs one state per wave, hence the row layout

@@ -46,6 +46,7 @@ struct FwdParams {
   int npw;                // states per wave: 1, or 2 (N >= 3; the output mode then stages one
                           // C.h partial per wave, and two workgroups share a CU)
   bool euler;             // Bbar = Delta * B instead of the zero-order hold
+  bool structured;        // the caller states A[d, n] = c_d a_n (SSCAN_FLAG_STRUCTURED_A)
 };
 
 // Sizes passed by value to the forward kernels (pointers go as separate

@@ -85,15 +85,16 @@ def test_unknown_dtype_is_unsupported(lib):
     assert fwd(lib, dtype=7) == 2
 
 
-@pytest.mark.parametrize("flags", [2, 0x80000000, 3])
+@pytest.mark.parametrize("flags", [4, 0x80000000, 7])
 def test_unknown_flag_bits_are_unsupported(lib, flags):
     assert fwd(lib, flags=flags) == 2
     assert b"flag" in lib.sscan_last_error()
 
 
-def test_header_defines_euler_flag():
+def test_header_defines_the_flags():
     text = open(HEADER).read()
     assert re.search(r"#define SSCAN_FLAG_EULER 1u", text)
+    assert re.search(r"#define SSCAN_FLAG_STRUCTURED_A 2u", text)
 
 
 @pytest.mark.parametrize("kw", [dict(batch=-1), dict(L=-3), dict(dim=-2)])
