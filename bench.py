@@ -99,13 +99,13 @@ def summarize_counters(fetch_csv: str, write_csv: str) -> dict:
     # the 512 MiB copy: 2^27 floats, four per thread
     calib = " grid=%d" % (COPY_ELEMS // 4)
     pick = lambda tab: next(v for k, v in tab.items() if "AUnaryFunctor" in k and k.endswith(calib))
-    # the forward kernel in its output mode (2nd template argument 0) with the
-    # zero-order hold (last argument false)
+    # the forward kernel in its output mode (template arguments <Tin, MODE, NFIX, EULER,
+    # STRUCT>: MODE 0, the zero-order hold, the general staging)
     def zoh(k):
         if "sscan::fwd_row_kernel<" not in k:
             return False
         args = [a.strip() for a in k.split("(")[0].split("<", 1)[1].rstrip(">").split(",")]
-        return args[1] == "0" and args[-1] == "false"
+        return args[1] == "0" and args[3] == "false" and (len(args) < 5 or args[4] == "false")
     copy_bytes = COPY_ELEMS * 4
     ff = copy_bytes / (pick(fetch) * 1024)
     fw = copy_bytes / (pick(write) * 1024)
