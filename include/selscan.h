@@ -130,11 +130,11 @@ size_t sscan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int6
  * last_state receives the initial state (zeros when absent).
  * Alignment: dtype-size alignment for token tensors, 4 bytes for float32 ones.
  */
-int sscan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
-              unsigned int flags, const void* x, const void* delta, const float* A, const void* B, const void* C,
-              const float* D, const void* z, const float* delta_bias,
-              const float* initial_state, void* y, float* last_state,
-              void* workspace, size_t workspace_bytes, void* stream);
+sscan_status sscan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+                       unsigned int flags, const void* x, const void* delta, const float* A, const void* B, const void* C,
+                       const float* D, const void* z, const float* delta_bias,
+                       const float* initial_state, void* y, float* last_state,
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Same as sscan_fwd, with the number of sequence segments chosen by the caller
@@ -143,12 +143,12 @@ int sscan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dt
  * For tuning and testing the two-level split; results agree with sscan_fwd
  * up to float32 rounding.
  */
-int sscan_fwd_segmented(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
-                        unsigned int flags, const void* x, const void* delta, const float* A, const void* B,
-                        const void* C, const float* D, const void* z, const float* delta_bias,
-                        const float* initial_state, void* y, float* last_state,
-                        void* workspace, size_t workspace_bytes, int64_t num_segments,
-                        void* stream);
+sscan_status sscan_fwd_segmented(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+                                 unsigned int flags, const void* x, const void* delta, const float* A, const void* B,
+                                 const void* C, const float* D, const void* z, const float* delta_bias,
+                                 const float* initial_state, void* y, float* last_state,
+                                 void* workspace, size_t workspace_bytes, int64_t num_segments,
+                                 void* stream);
 
 /*
  * sscan_fwd for callers that cannot allocate device memory: code under HIP graph
@@ -165,11 +165,11 @@ int sscan_fwd_segmented(int64_t batch, int64_t seqlen, int64_t dim, int64_t dsta
  * threads) race on it and must be serialized by the caller.
  */
 #define SSCAN_NOALLOC_SCRATCH_BYTES (32u << 20)
-int sscan_fwd_noalloc(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
-                      unsigned int flags, const void* x, const void* delta, const float* A,
-                      const void* B, const void* C, const float* D, const void* z,
-                      const float* delta_bias, const float* initial_state, void* y,
-                      float* last_state, void* stream);
+sscan_status sscan_fwd_noalloc(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+                               unsigned int flags, const void* x, const void* delta, const float* A,
+                               const void* B, const void* C, const float* D, const void* z,
+                               const float* delta_bias, const float* initial_state, void* y,
+                               float* last_state, void* stream);
 
 /*
  * One recurrent step for a single token per batch row (decode).
@@ -183,10 +183,10 @@ int sscan_fwd_noalloc(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate
  * Optional (NULL allowed): D, z, delta_bias.  Equivalent to sscan_fwd with
  * seqlen = 1, initial_state = last_state = state.
  */
-int sscan_step(int64_t batch, int64_t dim, int64_t dstate, int dtype, unsigned int flags,
-               float* state, const void* x, const void* delta, const float* A,
-               const void* B, const void* C, const float* D, const void* z,
-               const float* delta_bias, void* y, void* stream);
+sscan_status sscan_step(int64_t batch, int64_t dim, int64_t dstate, int dtype, unsigned int flags,
+                        float* state, const void* x, const void* delta, const float* A,
+                        const void* B, const void* C, const float* D, const void* z,
+                        const float* delta_bias, void* y, void* stream);
 
 /*
  * sscan_fwd with the short convolution that precedes the scan in a Mamba block,
@@ -210,13 +210,13 @@ int sscan_step(int64_t batch, int64_t dim, int64_t dstate, int dtype, unsigned i
  * 1 <= dconv <= SSCAN_MAX_DCONV (else SSCAN_ERR_UNSUPPORTED).  The backward pass does
  * not include the convolution: sscan_bwd differentiates the scan with respect to u.
  */
-int sscan_fwd_conv(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int64_t dconv,
-                   int dtype, unsigned int flags, const void* x, const float* conv_w,
-                   const float* conv_b, const float* conv_state_in, float* conv_state_out,
-                   const void* delta, const float* A, const void* B, const void* C,
-                   const float* D, const void* z, const float* delta_bias,
-                   const float* initial_state, void* y, float* last_state, void* workspace,
-                   size_t workspace_bytes, void* stream);
+sscan_status sscan_fwd_conv(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int64_t dconv,
+                            int dtype, unsigned int flags, const void* x, const float* conv_w,
+                            const float* conv_b, const float* conv_state_in, float* conv_state_out,
+                            const void* delta, const float* A, const void* B, const void* C,
+                            const float* D, const void* z, const float* delta_bias,
+                            const float* initial_state, void* y, float* last_state, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /*
  * sscan_step with the convolution prologue: the page-3 report's MambaBlock.step
@@ -229,11 +229,11 @@ int sscan_fwd_conv(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, i
  *   x          : [batch, dim] (dtype) raw input
  *   conv_w, conv_b, dconv: as sscan_fwd_conv; other arguments: as sscan_step.
  */
-int sscan_step_conv(int64_t batch, int64_t dim, int64_t dstate, int64_t dconv, int dtype,
-                    unsigned int flags, float* state, float* conv_state, const void* x,
-                    const float* conv_w, const float* conv_b, const void* delta, const float* A,
-                    const void* B, const void* C, const float* D, const void* z,
-                    const float* delta_bias, void* y, void* stream);
+sscan_status sscan_step_conv(int64_t batch, int64_t dim, int64_t dstate, int64_t dconv, int dtype,
+                             unsigned int flags, float* state, float* conv_state, const void* x,
+                             const float* conv_w, const float* conv_b, const void* delta, const float* A,
+                             const void* B, const void* C, const float* D, const void* z,
+                             const float* delta_bias, void* y, void* stream);
 
 /*
  * Workspace bytes sscan_bwd needs for a shape (0 for an empty problem).  The
@@ -282,13 +282,13 @@ size_t sscan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int6
  * Outputs must not overlap inputs, each other or the workspace.  Reductions run
  * in a fixed order: results are bitwise reproducible.
  */
-int sscan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
-              unsigned int flags, const void* x, const void* delta, const float* A, const void* B,
-              const void* C, const float* D, const void* z, const float* delta_bias,
-              const float* initial_state, const void* dy, const float* dlast_state, void* dx,
-              void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz,
-              float* ddelta_bias, float* dinitial_state, void* workspace, size_t workspace_bytes,
-              void* stream);
+sscan_status sscan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+                       unsigned int flags, const void* x, const void* delta, const float* A, const void* B,
+                       const void* C, const float* D, const void* z, const float* delta_bias,
+                       const float* initial_state, const void* dy, const float* dlast_state, void* dx,
+                       void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz,
+                       float* ddelta_bias, float* dinitial_state, void* workspace, size_t workspace_bytes,
+                       void* stream);
 
 /*
  * Saved checkpoints for a training step.  The lengnian.github.io notes ("Part3:
@@ -316,12 +316,12 @@ size_t sscan_checkpoint_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_
  * prologue here: the backward pass does not cover it).  y and last_state equal
  * sscan_fwd's bit for bit.
  */
-int sscan_fwd_checkpointed(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
-                           unsigned int flags, const void* x, const void* delta, const float* A,
-                           const void* B, const void* C, const float* D, const void* z,
-                           const float* delta_bias, const float* initial_state, void* y,
-                           float* last_state, void* workspace, size_t workspace_bytes,
-                           float* checkpoints, size_t checkpoint_bytes, void* stream);
+sscan_status sscan_fwd_checkpointed(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+                                    unsigned int flags, const void* x, const void* delta, const float* A,
+                                    const void* B, const void* C, const float* D, const void* z,
+                                    const float* delta_bias, const float* initial_state, void* y,
+                                    float* last_state, void* workspace, size_t workspace_bytes,
+                                    float* checkpoints, size_t checkpoint_bytes, void* stream);
 
 /* Workspace bytes sscan_bwd_checkpointed needs: sscan_bwd's less the checkpoint array. */
 size_t sscan_bwd_checkpointed_workspace_size(int64_t batch, int64_t seqlen, int64_t dim,
@@ -338,14 +338,14 @@ size_t sscan_bwd_checkpointed_workspace_size(int64_t batch, int64_t seqlen, int6
  * sscan_bwd's to rounding: sscan_bwd's own recomputation may split the sequence
  * differently from the forward, which rounds the states differently.
  */
-int sscan_bwd_checkpointed(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
-                           unsigned int flags, const void* x, const void* delta, const float* A,
-                           const void* B, const void* C, const float* D, const void* z,
-                           const float* delta_bias, const float* checkpoints,
-                           size_t checkpoint_bytes, const void* dy, const float* dlast_state,
-                           void* dx, void* ddelta, float* dA, void* dB, void* dC, float* dD,
-                           void* dz, float* ddelta_bias, float* dinitial_state, void* workspace,
-                           size_t workspace_bytes, void* stream);
+sscan_status sscan_bwd_checkpointed(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+                                    unsigned int flags, const void* x, const void* delta, const float* A,
+                                    const void* B, const void* C, const float* D, const void* z,
+                                    const float* delta_bias, const float* checkpoints,
+                                    size_t checkpoint_bytes, const void* dy, const float* dlast_state,
+                                    void* dx, void* ddelta, float* dA, void* dB, void* dC, float* dD,
+                                    void* dz, float* ddelta_bias, float* dinitial_state, void* workspace,
+                                    size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -609,12 +609,12 @@ size_t sscan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int6
   return seg_workspace_bytes(batch, dim, dstate, pl.nseg);
 }
 
-int sscan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype, unsigned int flags,
-              const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
-              const void* z, const float* delta_bias, const float* initial_state, void* y, float* last_state,
-              void* workspace, size_t workspace_bytes, void* stream) {
-  return fwd_impl(batch, seqlen, dim, dstate, dtype, flags, x, delta, A, B, C, D, z, delta_bias, initial_state, y,
-                  last_state, workspace, workspace_bytes, 0, stream, ConvArgs{});
+sscan_status sscan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype, unsigned int flags,
+                       const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
+                       const void* z, const float* delta_bias, const float* initial_state, void* y, float* last_state,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return static_cast<sscan_status>(fwd_impl(batch, seqlen, dim, dstate, dtype, flags, x, delta, A, B, C, D, z, delta_bias, initial_state, y,
+                  last_state, workspace, workspace_bytes, 0, stream, ConvArgs{}));
 }
 
 size_t sscan_checkpoint_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
@@ -622,74 +622,74 @@ size_t sscan_checkpoint_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_
   return checkpoint_bytes(batch, seqlen, dim, dstate);
 }
 
-int sscan_fwd_checkpointed(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
-                           unsigned int flags, const void* x, const void* delta, const float* A, const void* B,
-                           const void* C, const float* D, const void* z, const float* delta_bias,
-                           const float* initial_state, void* y, float* last_state, void* workspace,
-                           size_t workspace_bytes, float* checkpoints, size_t checkpoint_bytes_, void* stream) {
+sscan_status sscan_fwd_checkpointed(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+                                    unsigned int flags, const void* x, const void* delta, const float* A, const void* B,
+                                    const void* C, const float* D, const void* z, const float* delta_bias,
+                                    const float* initial_state, void* y, float* last_state, void* workspace,
+                                    size_t workspace_bytes, float* checkpoints, size_t checkpoint_bytes_, void* stream) {
   if (!checkpoints && batch > 0 && seqlen > 0 && dim > 0)
-    return fail(SSCAN_ERR_INVALID_ARG, "null required pointer (checkpoints)");
-  return fwd_impl(batch, seqlen, dim, dstate, dtype, flags, x, delta, A, B, C, D, z, delta_bias, initial_state, y,
-                  last_state, workspace, workspace_bytes, 0, stream, ConvArgs{}, checkpoints, checkpoint_bytes_);
+    return static_cast<sscan_status>(fail(SSCAN_ERR_INVALID_ARG, "null required pointer (checkpoints)"));
+  return static_cast<sscan_status>(fwd_impl(batch, seqlen, dim, dstate, dtype, flags, x, delta, A, B, C, D, z, delta_bias, initial_state, y,
+                  last_state, workspace, workspace_bytes, 0, stream, ConvArgs{}, checkpoints, checkpoint_bytes_));
 }
 
-int sscan_fwd_conv(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int64_t dconv, int dtype,
-                   unsigned int flags, const void* x, const float* conv_w, const float* conv_b,
-                   const float* conv_state_in, float* conv_state_out, const void* delta, const float* A,
-                   const void* B, const void* C, const float* D, const void* z, const float* delta_bias,
-                   const float* initial_state, void* y, float* last_state, void* workspace, size_t workspace_bytes,
-                   void* stream) {
-  if (!conv_w) return fail(SSCAN_ERR_INVALID_ARG, "null required pointer (conv_w)");
-  return fwd_impl(batch, seqlen, dim, dstate, dtype, flags, x, delta, A, B, C, D, z, delta_bias, initial_state, y,
+sscan_status sscan_fwd_conv(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int64_t dconv, int dtype,
+                            unsigned int flags, const void* x, const float* conv_w, const float* conv_b,
+                            const float* conv_state_in, float* conv_state_out, const void* delta, const float* A,
+                            const void* B, const void* C, const float* D, const void* z, const float* delta_bias,
+                            const float* initial_state, void* y, float* last_state, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (!conv_w) return static_cast<sscan_status>(fail(SSCAN_ERR_INVALID_ARG, "null required pointer (conv_w)"));
+  return static_cast<sscan_status>(fwd_impl(batch, seqlen, dim, dstate, dtype, flags, x, delta, A, B, C, D, z, delta_bias, initial_state, y,
                   last_state, workspace, workspace_bytes, 0, stream,
-                  ConvArgs{dconv, conv_w, conv_b, conv_state_in, conv_state_out});
+                  ConvArgs{dconv, conv_w, conv_b, conv_state_in, conv_state_out}));
 }
 
-int sscan_fwd_noalloc(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype, unsigned int flags,
-                      const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
-                      const void* z, const float* delta_bias, const float* initial_state, void* y,
-                      float* last_state, void* stream) {
+sscan_status sscan_fwd_noalloc(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype, unsigned int flags,
+                               const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
+                               const void* z, const float* delta_bias, const float* initial_state, void* y,
+                               float* last_state, void* stream) {
   // the split sscan_fwd would choose with an unlimited workspace; rejected if its
   // scratch exceeds the static array (nothing is launched then)
   const size_t need = sscan_fwd_workspace_size(batch, seqlen, dim, dstate, dtype);
   if (need > SSCAN_NOALLOC_SCRATCH_BYTES)
-    return fail(SSCAN_ERR_INVALID_ARG,
+    return static_cast<sscan_status>(fail(SSCAN_ERR_INVALID_ARG,
                 "sscan_fwd_noalloc: this shape needs %zu bytes of scratch, above the static %zu "
                 "(SSCAN_NOALLOC_SCRATCH_BYTES); use sscan_fwd with a workspace",
-                need, static_cast<size_t>(SSCAN_NOALLOC_SCRATCH_BYTES));
+                need, static_cast<size_t>(SSCAN_NOALLOC_SCRATCH_BYTES)));
   void* ws = nullptr;
   if (need > 0) {
     int rc = SSCAN_OK;
     ws = noalloc_scratch(&rc);
-    if (!ws) return rc;
+    if (!ws) return static_cast<sscan_status>(rc);
   }
-  return fwd_impl(batch, seqlen, dim, dstate, dtype, flags, x, delta, A, B, C, D, z, delta_bias, initial_state, y,
-                  last_state, ws, ws ? static_cast<size_t>(SSCAN_NOALLOC_SCRATCH_BYTES) : 0, 0, stream, ConvArgs{});
+  return static_cast<sscan_status>(fwd_impl(batch, seqlen, dim, dstate, dtype, flags, x, delta, A, B, C, D, z, delta_bias, initial_state, y,
+                  last_state, ws, ws ? static_cast<size_t>(SSCAN_NOALLOC_SCRATCH_BYTES) : 0, 0, stream, ConvArgs{}));
 }
 
-int sscan_fwd_segmented(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
-                        unsigned int flags, const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
-                        const void* z, const float* delta_bias, const float* initial_state, void* y,
-                        float* last_state, void* workspace, size_t workspace_bytes, int64_t num_segments,
-                        void* stream) {
-  return fwd_impl(batch, seqlen, dim, dstate, dtype, flags, x, delta, A, B, C, D, z, delta_bias, initial_state, y,
-                  last_state, workspace, workspace_bytes, num_segments, stream, ConvArgs{});
+sscan_status sscan_fwd_segmented(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+                                 unsigned int flags, const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
+                                 const void* z, const float* delta_bias, const float* initial_state, void* y,
+                                 float* last_state, void* workspace, size_t workspace_bytes, int64_t num_segments,
+                                 void* stream) {
+  return static_cast<sscan_status>(fwd_impl(batch, seqlen, dim, dstate, dtype, flags, x, delta, A, B, C, D, z, delta_bias, initial_state, y,
+                  last_state, workspace, workspace_bytes, num_segments, stream, ConvArgs{}));
 }
 
-int sscan_step(int64_t batch, int64_t dim, int64_t dstate, int dtype, unsigned int flags, float* state,
-               const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
-               const void* z, const float* delta_bias, void* y, void* stream) {
-  return step_impl(batch, dim, dstate, dtype, flags, state, x, delta, A, B, C, D, z, delta_bias, y, stream, 0, nullptr,
-                   nullptr, nullptr);
+sscan_status sscan_step(int64_t batch, int64_t dim, int64_t dstate, int dtype, unsigned int flags, float* state,
+                        const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
+                        const void* z, const float* delta_bias, void* y, void* stream) {
+  return static_cast<sscan_status>(step_impl(batch, dim, dstate, dtype, flags, state, x, delta, A, B, C, D, z, delta_bias, y, stream, 0, nullptr,
+                   nullptr, nullptr));
 }
 
-int sscan_step_conv(int64_t batch, int64_t dim, int64_t dstate, int64_t dconv, int dtype, unsigned int flags,
-                    float* state, float* conv_state, const void* x, const float* conv_w, const float* conv_b,
-                    const void* delta, const float* A, const void* B, const void* C, const float* D, const void* z,
-                    const float* delta_bias, void* y, void* stream) {
-  if (!conv_w) return fail(SSCAN_ERR_INVALID_ARG, "null required pointer (conv_w)");
-  return step_impl(batch, dim, dstate, dtype, flags, state, x, delta, A, B, C, D, z, delta_bias, y, stream, dconv,
-                   conv_w, conv_b, conv_state);
+sscan_status sscan_step_conv(int64_t batch, int64_t dim, int64_t dstate, int64_t dconv, int dtype, unsigned int flags,
+                             float* state, float* conv_state, const void* x, const float* conv_w, const float* conv_b,
+                             const void* delta, const float* A, const void* B, const void* C, const float* D, const void* z,
+                             const float* delta_bias, void* y, void* stream) {
+  if (!conv_w) return static_cast<sscan_status>(fail(SSCAN_ERR_INVALID_ARG, "null required pointer (conv_w)"));
+  return static_cast<sscan_status>(step_impl(batch, dim, dstate, dtype, flags, state, x, delta, A, B, C, D, z, delta_bias, y, stream, dconv,
+                   conv_w, conv_b, conv_state));
 }
 
 size_t sscan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype) {
@@ -698,15 +698,15 @@ size_t sscan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int6
   return bwd_layout(batch, seqlen, dim, dstate).total;
 }
 
-int sscan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype, unsigned int flags,
-              const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
-              const void* z, const float* delta_bias, const float* initial_state, const void* dy,
-              const float* dlast_state, void* dx, void* ddelta, float* dA, void* dB, void* dC, float* dD,
-              void* dz, float* ddelta_bias, float* dinitial_state, void* workspace, size_t workspace_bytes,
-              void* stream) {
-  return bwd_impl(batch, seqlen, dim, dstate, dtype, flags, x, delta, A, B, C, D, z, delta_bias, initial_state, dy,
+sscan_status sscan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype, unsigned int flags,
+                       const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
+                       const void* z, const float* delta_bias, const float* initial_state, const void* dy,
+                       const float* dlast_state, void* dx, void* ddelta, float* dA, void* dB, void* dC, float* dD,
+                       void* dz, float* ddelta_bias, float* dinitial_state, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  return static_cast<sscan_status>(bwd_impl(batch, seqlen, dim, dstate, dtype, flags, x, delta, A, B, C, D, z, delta_bias, initial_state, dy,
                   dlast_state, dx, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dinitial_state, workspace,
-                  workspace_bytes, stream);
+                  workspace_bytes, stream));
 }
 
 size_t sscan_bwd_checkpointed_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype) {
@@ -715,15 +715,15 @@ size_t sscan_bwd_checkpointed_workspace_size(int64_t batch, int64_t seqlen, int6
   return bwd_layout(batch, seqlen, dim, dstate).total_saved;
 }
 
-int sscan_bwd_checkpointed(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype, unsigned int flags,
-                           const void* x, const void* delta, const float* A, const void* B, const void* C,
-                           const float* D, const void* z, const float* delta_bias, const float* checkpoints,
-                           size_t checkpoint_bytes_, const void* dy, const float* dlast_state, void* dx,
-                           void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz, float* ddelta_bias,
-                           float* dinitial_state, void* workspace, size_t workspace_bytes, void* stream) {
-  return bwd_impl(batch, seqlen, dim, dstate, dtype, flags, x, delta, A, B, C, D, z, delta_bias, nullptr, dy,
+sscan_status sscan_bwd_checkpointed(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype, unsigned int flags,
+                                    const void* x, const void* delta, const float* A, const void* B, const void* C,
+                                    const float* D, const void* z, const float* delta_bias, const float* checkpoints,
+                                    size_t checkpoint_bytes_, const void* dy, const float* dlast_state, void* dx,
+                                    void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz, float* ddelta_bias,
+                                    float* dinitial_state, void* workspace, size_t workspace_bytes, void* stream) {
+  return static_cast<sscan_status>(bwd_impl(batch, seqlen, dim, dstate, dtype, flags, x, delta, A, B, C, D, z, delta_bias, nullptr, dy,
                   dlast_state, dx, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dinitial_state, workspace,
-                  workspace_bytes, stream, checkpoints, checkpoint_bytes_, true);
+                  workspace_bytes, stream, checkpoints, checkpoint_bytes_, true));
 }
 
 }  // extern "C"
