@@ -167,7 +167,92 @@ __global__ __launch_bounds__(256) void step_kernel(float* __restrict__ S, const 
   }
 }
 
+// The decode step for N = 16 with vector-aligned tensors and no convolution prologue:
+// 4 lanes per (b, d) row and 4 states per lane, as step_kernel<.., 4, 4, true, 16, ..>,
+// but each thread walks KB batch rows of one channel, so A[d] (and 1/A) is loaded once
+// per KB rows instead of once per row: with A read per row, every step moved the whole
+// [D, N] A (327 KB at dim 5120) through L2 once per batch row, as much traffic as the
+// state itself.  The KB state quads are loaded before any is used.
+template <typename Tin, bool EULER, int KB>
+__global__ __launch_bounds__(256) void step16_kernel(float* __restrict__ S, const Tin* __restrict__ X,
+                                                     const Tin* __restrict__ DT, const Tin* __restrict__ Z,
+                                                     const Tin* __restrict__ Bp, const Tin* __restrict__ Cp,
+                                                     const float* __restrict__ Ag, const float* __restrict__ Dg,
+                                                     const float* __restrict__ biasg, Tin* __restrict__ Y,
+                                                     int64_t groups, int64_t dim) {
+  constexpr int N = 16;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t rg = gid >> 2;               // (batch group, channel)
+  const int q = static_cast<int>(gid & 3);   // lane of the row: states 4q .. 4q + 3
+  if (rg >= groups * dim) return;            // whole rows leave together
+  const int64_t bg = rg / dim, d = rg - bg * dim;
+  const int n0 = 4 * q;
+
+  const float4 av = *reinterpret_cast<const float4*>(Ag + d * N + n0);
+  const float a[4] = {av.x, av.y, av.z, av.w};
+  float rA[4];
+  bool small = false;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    rA[j] = a[j] != 0.f ? hw_rcp(a[j]) : 0.f;
+    small = small || fabsf(a[j]) < kSmallA;
+  }
+  const bool accurate = !EULER && __any(small);
+  const float bias2 = biasg ? biasg[d] * kLog2e : 0.f;
+  const float dsk = Dg ? Dg[d] : 0.f;
+
+  float4 hq[KB];
+#pragma unroll
+  for (int k = 0; k < KB; ++k) hq[k] = load_state4(S + ((bg * KB + k) * dim + d) * N + n0);
+#pragma unroll
+  for (int k = 0; k < KB; ++k) {
+    const int64_t b = bg * KB + k;
+    const int64_t row = b * dim + d;
+    const float xv = to_f32(X[row]);
+    float bv[4], cv[4];
+    load4<Tin, true>(Bp + b * N + n0, n0, N, bv);
+    load4<Tin, true>(Cp + b * N + n0, n0, N, cv);
+    const float d2 = softplus_log2e(fmaf(to_f32(DT[row]), kLog2e, bias2));  // Delta * log2(e)
+    const float dl = d2 * kLn2;
+    float h[4] = {hq[k].x, hq[k].y, hq[k].z, hq[k].w};
+    float yp = 0.f;
+    auto update = [&](auto acc) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float arg = d2 * a[j];
+        const float e = hw_exp2(arg);
+        const float g = EULER ? dl : (decltype(acc)::value ? zoh_phi(e, arg, d2, rA[j]) : (e - 1.f) * rA[j]);
+        h[j] = fmaf(e, h[j], g * bv[j] * xv);
+        yp = fmaf(cv[j], h[j], yp);
+      }
+    };
+    if (accurate)
+      update(std::true_type{});
+    else
+      update(std::false_type{});
+    store_state4(S + row * N + n0, h[0], h[1], h[2], h[3]);
+    yp += __shfl_xor(yp, 1);
+    yp += __shfl_xor(yp, 2);
+    if (q == 0) {
+      float yv = yp + dsk * xv;
+      if (Z) yv *= silu(to_f32(Z[row]));
+      store_val(&Y[row], yv);
+    }
+  }
+}
+
 namespace {
+
+template <typename Tin, bool EU>
+void launch_step16(const StepParams& p, hipStream_t s) {
+  constexpr int KB = 4;
+  const int64_t groups = p.batch / KB;
+  const int64_t threads = groups * p.dim * 4;
+  hipLaunchKernelGGL((step16_kernel<Tin, EU, KB>), dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0,
+                     s, p.state, static_cast<const Tin*>(p.x), static_cast<const Tin*>(p.dt),
+                     static_cast<const Tin*>(p.z), static_cast<const Tin*>(p.B), static_cast<const Tin*>(p.C), p.A,
+                     p.Dskip, p.bias, static_cast<Tin*>(p.y), groups, p.dim);
+}
 
 template <typename Tin, int SPL, int LPR, bool VEC, int NF, bool EU>
 void launch_step_one(const StepParams& p, hipStream_t s) {
@@ -189,7 +274,9 @@ void launch_step_one(const StepParams& p, hipStream_t s) {
 
 template <typename Tin, bool EU>
 void launch_step_t(const StepParams& p, bool vec, hipStream_t s) {
-  if (p.N == 16 && vec) {
+  if (p.N == 16 && vec && !p.conv_w && p.batch % 4 == 0) {
+    launch_step16<Tin, EU>(p, s);
+  } else if (p.N == 16 && vec) {
     // 4 states per lane: in-place float4 updates streamed at 5.4 TB/s against 5.0 with 8
     launch_step_one<Tin, 4, 4, true, 16, EU>(p, s);
   } else if (vec) {

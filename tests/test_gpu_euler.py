@@ -51,11 +51,11 @@ def test_euler_differs_from_zoh(ss):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("N", [4, 7, 12, 16])
-def test_euler_step(ss, orc, dtype, N):
+@pytest.mark.parametrize("N,Bt", [(4, 3), (7, 3), (12, 3), (16, 3), (16, 8)])
+def test_euler_step(ss, orc, dtype, N, Bt):
     import torch
-    rng = np.random.default_rng(400 + N)
-    Bt, Dm = 3, 130
+    rng = np.random.default_rng(400 + N + Bt)
+    Dm = 130
     note(f"[case] Euler step B={Bt} D={Dm} N={N} {dtype}")
     st0 = (0.3 * rng.standard_normal((Bt, Dm, N))).astype(np.float32)
     A = -(rng.uniform(0.5, 4, (Dm, N))).astype(np.float32)

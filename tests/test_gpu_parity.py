@@ -316,11 +316,12 @@ def test_bf16_bc_two_byte_aligned(ss, orc, N):
 # single-token step
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("N", [1, 3, 4, 5, 8, 12, 16])
-def test_step_small(ss, orc, dtype, N):
+@pytest.mark.parametrize("N,Bt", [(1, 3), (3, 3), (4, 3), (5, 3), (8, 3), (12, 3), (16, 3), (16, 8)])
+def test_step_small(ss, orc, dtype, N, Bt):
+    # N = 16 with a batch divisible by 4 runs the kernel that walks 4 batch rows per thread
     import torch
-    rng = np.random.default_rng(200 + N)
-    Bt, Dm = 3, 130
+    rng = np.random.default_rng(200 + N + Bt)
+    Dm = 130
     note(f"[case] step B={Bt} D={Dm} N={N} {dtype}")
     st0 = (0.3 * rng.standard_normal((Bt, Dm, N))).astype(np.float32)
     A = -(rng.uniform(0.5, 4, (Dm, N))).astype(np.float32)

@@ -124,10 +124,12 @@ def test_small_A_conv_prologue(ss, orc):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_small_A_decode_steps(ss, orc, dtype):
+@pytest.mark.parametrize("Bt", [2, 4])
+def test_small_A_decode_steps(ss, orc, dtype, Bt):
+    # batch 4: the N = 16 kernel that walks 4 batch rows per thread
     import torch
-    rng = np.random.default_rng(620)
-    Bt, Dm, N, steps = 2, 72, 16, 300
+    rng = np.random.default_rng(620 + Bt)
+    Dm, N, steps = 72, 16, 300
     A = -(np.arange(1, N + 1, dtype=np.float32))[None, :].repeat(Dm, 0)
     for i, a in enumerate(SMALL):
         A[i, :] = a
