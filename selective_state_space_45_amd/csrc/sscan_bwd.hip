@@ -392,52 +392,61 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(
         unpack(sCw[t * (NSP / S)], cq);
         const float delta = d2 * kLn2;
         float r1 = 0.f, r2 = 0.f;
+        // both states of the step in one block, behind one wave-uniform branch per step
+        // (a branch per state kept the two states' chains from interleaving and cost a
+        // taken branch and a jump per state-step on the fast path)
+        auto states = [&](auto slowc) __attribute__((always_inline)) {
+          constexpr bool SLOW = decltype(slowc)::value;
 #pragma unroll
-        for (int q = 0; q < S; ++q) {
-          const float a = ahist[q][t];
-          const float hp = hist[q][t];
-          const float gh = fmaf(go, cq[q], G[q]);
-          const float bx = bq[q] * xv;
-          // hn = h_l, the state after the step: h_l = Abar h_{l-1} + phi B x
-          const float hn = (t + 1 < T) ? hist[q][t + 1] : h[q];
-          float gphi;
-          const float Gn = a * gh;
-          if constexpr (EULER) {
-            gphi = gh * delta;
-            r2 = fmaf(gh, fmaf(An[q] * a, hp, bx), r2);
-            gA[q] = fmaf(gh, delta * a * hp, gA[q]);
-          } else {
-            // d h_l / d Delta = Abar (A h_{l-1} + B x) = A hn + B x in both cases, formed
-            // before the A = 0 branch so that the two branches share its registers
-            r2 = fmaf(gh, fmaf(An[q], hn, bx), r2);
-            if (!smallA) {
-              // d h_l / d A = Delta Abar (h_{l-1} + k) - phi k = Delta (hn + k) - phi k
-              // with k = B x / A; gh phi = (Abar gh - gh) / A, so phi is never formed.
-              // The term (Delta Abar - phi) k cancels for small Delta A, but only down
-              // to a few ulp of Delta k, the size of the leading term
-              gphi = (Gn - gh) * iAn[q];
-              const float k = bx * iAn[q];
-              gA[q] = fmaf(delta, gh * (hn + k), gA[q]);
-              gA[q] = fmaf(-gphi, k, gA[q]);
+          for (int q = 0; q < S; ++q) {
+            const float a = ahist[q][t];
+            const float hp = hist[q][t];
+            const float gh = fmaf(go, cq[q], G[q]);
+            const float bx = bq[q] * xv;
+            // hn = h_l, the state after the step: h_l = Abar h_{l-1} + phi B x
+            const float hn = (t + 1 < T) ? hist[q][t + 1] : h[q];
+            float gphi;
+            const float Gn = a * gh;
+            if constexpr (EULER) {
+              gphi = gh * delta;
+              r2 = fmaf(gh, fmaf(An[q] * a, hp, bx), r2);
+              gA[q] = fmaf(gh, delta * a * hp, gA[q]);
             } else {
-              const float phi = zoh_phi(a, d2 * An[q], d2, iAn[q]);
-              gphi = gh * phi;
-              // a wave with some small |A|: dphi/dA = Delta^2 (u e^u - e^u + 1)/u^2,
-              // u = Delta A, from its series for |u| < 0.5 and its closed form
-              // otherwise; both are computed (each finite everywhere) and blended, so
-              // no per-lane branch splits the step
-              const float u = delta * An[q];
-              const float ser = delta * delta * dphi1_series(fmaxf(fminf(u, 0.5f), -0.5f));
-              const float dir = (delta * a - phi) * iAn[q];
-              const float wsel = (fabsf(u) < 0.5f) ? 1.f : 0.f;
-              const float dphi_dA = fmaf(wsel, ser - dir, dir);
-              gA[q] = fmaf(gh, fmaf(delta * a, hp, dphi_dA * bx), gA[q]);
+              // d h_l / d Delta = Abar (A h_{l-1} + B x) = A hn + B x in both forms
+              r2 = fmaf(gh, fmaf(An[q], hn, bx), r2);
+              if constexpr (!SLOW) {
+                // d h_l / d A = Delta Abar (h_{l-1} + k) - phi k = Delta (hn + k) - phi k
+                // with k = B x / A; gh phi = (Abar gh - gh) / A, so phi is never formed.
+                // The term (Delta Abar - phi) k cancels for small Delta A, but only down
+                // to a few ulp of Delta k, the size of the leading term
+                gphi = (Gn - gh) * iAn[q];
+                const float k = bx * iAn[q];
+                gA[q] = fmaf(delta, gh * (hn + k), gA[q]);
+                gA[q] = fmaf(-gphi, k, gA[q]);
+              } else {
+                const float phi = zoh_phi(a, d2 * An[q], d2, iAn[q]);
+                gphi = gh * phi;
+                // a wave with some small |A|: dphi/dA = Delta^2 (u e^u - e^u + 1)/u^2,
+                // u = Delta A, from its series for |u| < 0.5 and its closed form
+                // otherwise; both are computed (each finite everywhere) and blended, so
+                // no per-lane branch splits the step
+                const float u = delta * An[q];
+                const float ser = delta * delta * dphi1_series(fmaxf(fminf(u, 0.5f), -0.5f));
+                const float dir = (delta * a - phi) * iAn[q];
+                const float wsel = (fabsf(u) < 0.5f) ? 1.f : 0.f;
+                const float dphi_dA = fmaf(wsel, ser - dir, dir);
+                gA[q] = fmaf(gh, fmaf(delta * a, hp, dphi_dA * bx), gA[q]);
+              }
             }
+            red[q * T + t] = gphi * xv;
+            r1 = fmaf(gphi, bq[q], r1);
+            G[q] = Gn;
           }
-          red[q * T + t] = gphi * xv;
-          r1 = fmaf(gphi, bq[q], r1);
-          G[q] = Gn;
-        }
+        };
+        if (EULER || !smallA)
+          states(std::false_type{});
+        else
+          states(std::true_type{});
         s_r1[w][t][lane] = r1;
         s_r2[w][t][lane] = r2;
         // dA is needed only after the last block; without this anchor the compiler
