@@ -412,18 +412,22 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(
               r2 = fmaf(gh, fmaf(An[q] * a, hp, bx), r2);
               gA[q] = fmaf(gh, delta * a * hp, gA[q]);
             } else {
-              // d h_l / d Delta = Abar (A h_{l-1} + B x) = A hn + B x in both forms
-              r2 = fmaf(gh, fmaf(An[q], hn, bx), r2);
               if constexpr (!SLOW) {
-                // d h_l / d A = Delta Abar (h_{l-1} + k) - phi k = Delta (hn + k) - phi k
-                // with k = B x / A; gh phi = (Abar gh - gh) / A, so phi is never formed.
-                // The term (Delta Abar - phi) k cancels for small Delta A, but only down
-                // to a few ulp of Delta k, the size of the leading term
+                // d h_l / d Delta = Abar (A h_{l-1} + B x) = A hn + B x = A (hn + k) and
+                // d h_l / d A = Delta Abar (h_{l-1} + k) - phi k = Delta (hn + k) - phi k,
+                // with k = B x / A: both terms share q = gh (hn + k).  gh phi = (Abar gh
+                // - gh) / A, so phi is never formed.  The term (Delta Abar - phi) k
+                // cancels for small Delta A, but only down to a few ulp of Delta k, the
+                // size of the leading term (this form serves |A| >= kSmallA only)
                 gphi = (Gn - gh) * iAn[q];
                 const float k = bx * iAn[q];
-                gA[q] = fmaf(delta, gh * (hn + k), gA[q]);
+                const float qh = gh * (hn + k);
+                r2 = fmaf(An[q], qh, r2);
+                gA[q] = fmaf(delta, qh, gA[q]);
                 gA[q] = fmaf(-gphi, k, gA[q]);
               } else {
+                // d h_l / d Delta = A hn + B x, formed directly (k = B x / A is large here)
+                r2 = fmaf(gh, fmaf(An[q], hn, bx), r2);
                 const float phi = zoh_phi(a, d2 * An[q], d2, iAn[q]);
                 gphi = gh * phi;
                 // a wave with some small |A|: dphi/dA = Delta^2 (u e^u - e^u + 1)/u^2,
