@@ -94,19 +94,54 @@ int64_t pick_segments(int64_t base, int64_t seqlen, int64_t per_round, int64_t m
   return best;
 }
 
+// Segment count of a split output-mode forward by a cost model: the passes run in
+// rounds of per_round workgroups (two per CU), each round as long as a segment plus
+// a fixed pipeline fill and drain of two chunks; a last round at most half full costs
+// 0.6 of a round (its workgroups have a CU each, and run faster).  Candidates run from
+// the count that fills 90 % of one round to eight times that, with segments of at
+// least four chunks, and segment lengths rounded up to whole chunks as the plan does;
+// on equal costs the fewest segments win.  The 0.6 was fitted to a sweep of 15 split
+// shapes (fp32 and bf16, 24 to 128 (batch, tile) workgroups, 1K to 128K steps), over
+// which the pick was the fastest count or within 4 % of it; the mamba130m layer
+// (batch 2, 2048 steps, dim 1536) gets 10 segments, 0.083 ms, where a rule that only
+// maximised the last round's fill took 16, 0.087 ms.
+int64_t pick_segments_out(int64_t base, int64_t seqlen, int64_t per_round) {
+  if (base <= 0 || base >= per_round / 2) return 1;
+  constexpr int64_t T = sscan::kChunk;
+  int64_t lo = (9 * per_round + 10 * base - 1) / (10 * base);
+  int64_t hi = 8 * lo;
+  const int64_t cap = seqlen / (4 * T) < 1024 ? seqlen / (4 * T) : 1024;
+  if (hi > cap) hi = cap;
+  if (lo > hi) lo = 1;
+  int64_t best = 1;
+  double best_cost = -1.0;
+  for (int64_t want = lo; want <= hi; ++want) {
+    int64_t len = (seqlen + want - 1) / want;
+    len = (len + T - 1) / T * T;
+    const int64_t nseg = (seqlen + len - 1) / len;
+    const int64_t wgs = base * nseg;
+    const int64_t full = wgs / per_round, rem = wgs % per_round;
+    const double rounds = static_cast<double>(full) + (rem == 0 ? 0.0 : (2 * rem <= per_round ? 0.6 : 1.0));
+    const double cost = rounds * static_cast<double>(len + 2 * T);
+    if (best_cost < 0.0 || cost < best_cost) {
+      best_cost = cost;
+      best = nseg;
+    }
+  }
+  return best;
+}
+
 // Segments of the forward.  A grid of at least one workgroup per CU runs unsplit.  A
 // smaller one is split, and its main pass then runs two states per wave, whose LDS use
-// lets two workgroups share a CU, so the split aims at rounds of 2 x CUs workgroups.
-// The checkpoint pass of the backward keeps one state per wave and one-per-CU rounds.
-// Output-mode segments are at least 8 chunks long: with 4-chunk segments the pipeline
-// fill of each segment outweighed the fuller last round (mamba130m layer, 48
-// workgroups: 16 segments 0.094 ms, 32 segments 0.099 ms).
+// lets two workgroups share a CU, so the split aims at rounds of 2 x CUs workgroups
+// (pick_segments_out).  The checkpoint pass of the backward keeps one state per wave
+// and one-per-CU rounds.
 int auto_segments(int64_t batch, int64_t seqlen, int64_t dim, int mode) {
   const int64_t base = (dim + sscan::kTile - 1) / sscan::kTile * batch;
   const int64_t cus = device_cus();
   if (base >= cus) return 1;
-  const bool out = mode == sscan::kFwdOut;
-  return static_cast<int>(pick_segments(base, seqlen, (out ? 2 : 1) * cus, (out ? 8 : 4) * sscan::kChunk));
+  if (mode == sscan::kFwdOut) return static_cast<int>(pick_segments_out(base, seqlen, 2 * cus));
+  return static_cast<int>(pick_segments(base, seqlen, cus, 4 * sscan::kChunk));
 }
 
 // States per wave of a forward launch of nwg workgroups: two once there are more

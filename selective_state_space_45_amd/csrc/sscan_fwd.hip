@@ -42,11 +42,26 @@ __global__ __launch_bounds__(256) void carry_kernel(const float* __restrict__ ag
   const int64_t d = bd % dim;
   const float a = A[d * N + n];
   float c = h_init ? h_init[i] : 0.f;
-  for (int s = 0; s < nseg; ++s) {
-    carry[static_cast<int64_t>(s) * total + i] = c;
-    if (s + 1 < nseg)
-      c = fmaf(hw_exp2(a * agg_s[static_cast<int64_t>(s) * batch * dim + bd]), c,
-               agg_h[static_cast<int64_t>(s) * total + i]);
+  // Segments in groups of G: the group's aggregates are loaded together, so their
+  // latencies overlap instead of adding up along the sequential combine.
+  constexpr int G = 8;
+  for (int s0 = 0; s0 < nseg; s0 += G) {
+    float hv[G], sv[G];
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      const int s = s0 + k;
+      const bool have = s + 1 < nseg;   // the last segment has no aggregate
+      hv[k] = have ? agg_h[static_cast<int64_t>(s) * total + i] : 0.f;
+      sv[k] = have ? agg_s[static_cast<int64_t>(s) * batch * dim + bd] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      const int s = s0 + k;
+      if (s < nseg) {
+        carry[static_cast<int64_t>(s) * total + i] = c;
+        c = fmaf(hw_exp2(a * sv[k]), c, hv[k]);
+      }
+    }
   }
 }
 

@@ -43,9 +43,9 @@
 namespace sscan {
 
 // B values of a wave's NPW states at one timestep, kept as raw scalar words.
-// PAIR: bf16 with even N and 4-byte aligned B and C, so the wave's states sit in one
-// aligned dword (NPW = 2: both halves; NPW = 1: the half `sel` picks).  Otherwise NPW
-// elements are loaded one by one.
+// PAIR: even N and B and C aligned to two elements, so the wave's states sit in one
+// aligned word (NPW = 2: both halves; NPW = 1: the half `sel` picks): a dword of two
+// bf16, or a 64-bit pair of fp32.  Otherwise NPW elements are loaded one by one.
 template <typename Tin, bool PAIR, int NPW>
 struct BRaw {
   Tin v[NPW];
@@ -76,10 +76,33 @@ struct BRaw<bf16_t, true, NPW> {
   __device__ __forceinline__ void clear_missing(const bool*) {}
 };
 
+// fp32 pairs: even N and 8-byte aligned B and C, so a wave's two states sit in one
+// aligned 64-bit word, read by one scalar load instead of two.
+template <int NPW>
+struct BRaw<float, true, NPW> {
+  float2 v;
+  __device__ __forceinline__ void load(const float* __restrict__ B, int64_t row, const int*) {
+    v = *reinterpret_cast<const float2*>(B + row);
+  }
+  __device__ __forceinline__ float get(int j, int sel) const {
+    if constexpr (NPW == 2) return j == 0 ? v.x : v.y;
+    return sel ? v.y : v.x;
+  }
+  __device__ __forceinline__ void clear_missing(const bool*) {}
+};
+
 // C row of one timestep (all N states) as float32, read through scalar loads.
 template <typename Tin, bool PAIR, int NMAX>
 __device__ __forceinline__ void load_c_row(const Tin* __restrict__ row, int N, float* c) {
-  if constexpr (PAIR) {
+  if constexpr (PAIR && std::is_same<Tin, float>::value) {
+    const float2* r64 = reinterpret_cast<const float2*>(row);
+#pragma unroll
+    for (int k = 0; k < NMAX / 2; ++k) {
+      const float2 wd = (2 * k < N) ? r64[k] : make_float2(0.f, 0.f);
+      c[2 * k] = wd.x;
+      c[2 * k + 1] = wd.y;
+    }
+  } else if constexpr (PAIR) {
     const uint32_t* r32 = reinterpret_cast<const uint32_t*>(row);
 #pragma unroll
     for (int k = 0; k < NMAX / 2; ++k) {
@@ -249,8 +272,32 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
   BRaw<Tin, PAIR, NPW> bc[T];
   BRaw<Tin, PAIR, NPW> cc[PART ? T : 1];
 
+  // Warm-up load of chunk c's B rows (and C rows in output mode) into the L2: the
+  // waves read them later through scalar loads issued half a chunk ahead, whose misses
+  // would otherwise wait on HBM.  One element per lane over the chunk's contiguous
+  // rows (NSPLIT * 64 lanes cover both arrays: NSPLIT * NPW >= N); the value is only
+  // kept alive, by the prologue that consumes the same chunk's x, dt and z.  Not in
+  // the convolution variant, whose code the compiler then fails to build.
+  Tin warm = Tin(0);
+  auto bcwarm = [&](int c) {
+    const int per = T * N;
+    const int e = w * 64 + lane;
+    const int rows = seg_n - c * T < T ? seg_n - c * T : T;
+    const bool isc = OUT && e >= per;
+    const int o = isc ? e - per : e;
+    if ((isc || e < per) && o < rows * N) {
+      const int64_t off = (b * L + l_begin + static_cast<int64_t>(c) * T) * N + o;
+      warm = isc ? Cg[off] : Bg[off];
+    }
+  };
+  auto keep_warm = [&]() {
+    float v = to_f32(warm);
+    asm volatile("" : "+v"(v));
+  };
+
   // Global loads of x, dt, z for this wave's prologue timesteps of chunk c.
   auto gload = [&](int c) {
+    if constexpr (!CONV) bcwarm(c);
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int l = c * T + w + NSPLIT * i;  // within the segment
@@ -357,6 +404,7 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
         ed[P][i] = dsk * xv;
       }
     }
+    keep_warm();
   };
 
   // PART: this wave's share of C.h after timestep t, to LDS for the epilogue.
@@ -612,9 +660,13 @@ hipError_t launch_fwd_variant(const FwdParams& p, bool bf16, hipStream_t s) {
   const int64_t nblocks = p.ndtiles * p.batch * (MODE == kFwdAgg ? (p.nseg - 1) : p.nseg);
   if (nblocks <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(nblocks));
-  const bool pair = bf16 && (p.N % 2 == 0) && ((reinterpret_cast<uintptr_t>(p.B) & 3) == 0) &&
-                    ((reinterpret_cast<uintptr_t>(p.C) & 3) == 0);
-  if (!bf16)
+  // two elements: 4 bytes for bf16, 8 for fp32
+  const uintptr_t amask = bf16 ? 3 : 7;
+  const bool pair = (p.N % 2 == 0) && ((reinterpret_cast<uintptr_t>(p.B) & amask) == 0) &&
+                    ((reinterpret_cast<uintptr_t>(p.C) & amask) == 0);
+  if (!bf16 && pair)
+    launch_by_n<float, MODE, true, EU, CV>(p, grid, s);
+  else if (!bf16)
     launch_by_n<float, MODE, false, EU, CV>(p, grid, s);
   else if (pair)
     launch_by_n<bf16_t, MODE, true, EU, CV>(p, grid, s);

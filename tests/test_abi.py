@@ -149,10 +149,13 @@ def test_workspace_size(lib):
     # a long single-row sequence is split: carry + end state + sums per segment
     ws = lib.sscan_fwd_workspace_size(1, 131072, 2560, 16, 1)
     assert ws > 0 and ws % (4 * 2560 * 33) == 0
-    # segment counts by round fill with two workgroups per CU (256 CUs): 40 workgroups
-    # x 64 segments = 5 full rounds of 512; 48 x 16 (segments >= 128 steps)
+    # segment counts by the round cost model with two workgroups per CU (256 CUs):
+    # 40 workgroups x 64 segments = 5 full rounds of 512 steps 2048; 48 x 10 = one round
+    # of 480 (the 16 that fill 1.5 rounds cost more: 1.6 x (128 + 32) > 208 + 32)
     assert ws == 64 * 4 * 2560 * 33
-    assert lib.sscan_fwd_workspace_size(2, 2048, 1536, 16, 0) == 16 * 4 * 2 * 1536 * 33
+    assert lib.sscan_fwd_workspace_size(2, 2048, 1536, 16, 0) == 10 * 4 * 2 * 1536 * 33
+    # batch 6, dim 1536, seqlen 65536: 144 workgroups x 32 segments = 9 full rounds
+    assert lib.sscan_fwd_workspace_size(6, 65536, 1536, 16, 1) == 32 * 4 * 6 * 1536 * 33
     assert lib.sscan_fwd_workspace_size(1, 0, 2560, 16, 1) == 0
 
 

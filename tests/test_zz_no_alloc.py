@@ -55,8 +55,8 @@ def test_noalloc_matches_fwd_two_calls(ss, orc):
 
 def test_noalloc_rejects_scratch_above_the_maximum(ss):
     lib = ss.library()
-    # batch 6, dim 1536 (24 channel tiles), seqlen 65536: the split's round fill picks
-    # enough segments that carries, end states and sums take 38.9 MB > 32 MiB
+    # batch 6, dim 1536 (24 channel tiles), seqlen 65536: the split picks 32 segments, so
+    # carries, end states and sums take 38.9 MB > 32 MiB
     need = ss.fwd_workspace_size(6, 65536, 1536, 16)
     assert need > (32 << 20), need
     P = ctypes.c_void_p
