@@ -245,12 +245,16 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
   }
   const Tin* __restrict__ Xrow = xg + b * L * dim + dtile * kTile;   // whole sequence of this row
 
-  Tin rx, rdt, rz, rbc;
-  Tin rxc[KC];
-  // Global loads of chunk c for the prologue: x, dt, z of timestep w (lane = channel)
-  // and this wave's B/C rows.  STEADY: chunk c is full.  Otherwise positions past the
-  // segment end read its last row (those steps become identities in the prologue).
-  auto gload = [&](auto steadyc, int c) __attribute__((always_inline)) {
+  // Two register sets for the global loads, by chunk parity: chunk c's loads are
+  // issued two iterations before its prologue consumes them.
+  Tin rx[2], rdt[2], rz[2], rbc[2];
+  Tin rxc[2][KC];
+  // Global loads of chunk c (parity S) for the prologue: x, dt, z of timestep w
+  // (lane = channel) and this wave's B/C rows.  STEADY: chunk c is full.  Otherwise
+  // positions past the segment end read its last row (those steps become identities
+  // in the prologue).
+  auto gload = [&](auto sc, auto steadyc, int c) __attribute__((always_inline)) {
+    constexpr int S = decltype(sc)::value;
     constexpr bool STEADY = decltype(steadyc)::value;
     const int l = c * T + w;
     const int64_t off = static_cast<int64_t>(STEADY ? l : (l < seg_n ? l : seg_n - 1)) * dim;
@@ -262,20 +266,20 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
       for (int k = 0; k < KC; ++k) {
         const int back = (K - 1 - k) < 0 ? 0 : (K - 1 - k);
         const int64_t pos = lg - (back <= lg ? back : lg);
-        rxc[k] = ld_off(Xrow + pos * dim, dlane);
+        rxc[S][k] = ld_off(Xrow + pos * dim, dlane);
       }
     } else {
-      rx = ld_off(Xb + off, dlane);
+      rx[S] = ld_off(Xb + off, dlane);
     }
-    rdt = ld_off(DTb + off, dlane);
-    if constexpr (OUT) rz = ld_off(Zb + off, dlane);
+    rdt[S] = ld_off(DTb + off, dlane);
+    if constexpr (OUT) rz[S] = ld_off(Zb + off, dlane);
     if (bcwave) {
       const int r0 = c * T + bcrow0;
       if constexpr (STEADY) {
-        rbc = ld_off(BCs + static_cast<int64_t>(r0) * N, bcoff);
+        rbc[S] = ld_off(BCs + static_cast<int64_t>(r0) * N, bcoff);
       } else {
         const int rr = r0 + bcj < seg_n ? r0 + bcj : seg_n - 1;
-        rbc = ld_off(BCs + static_cast<int64_t>(rr) * N, static_cast<unsigned>(bcn) * sizeof(Tin));
+        rbc[S] = ld_off(BCs + static_cast<int64_t>(rr) * N, static_cast<unsigned>(bcn) * sizeof(Tin));
       }
     }
   };
@@ -290,7 +294,7 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
       const int64_t l_glob = l_begin + c * T + w;
       float v[KC];
 #pragma unroll
-      for (int k = 0; k < KC; ++k) v[k] = to_f32(rxc[k]);
+      for (int k = 0; k < KC; ++k) v[k] = to_f32(rxc[P][k]);
       if (l_glob < K - 1) {   // wave-uniform: the window reaches before the sequence
 #pragma unroll
         for (int k = 0; k < KC; ++k) {
@@ -303,9 +307,9 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
       for (int k = 0; k < KC; ++k) acc = fmaf(cw[k], v[k], acc);
       xv = silu(acc);
     } else {
-      xv = to_f32(rx);
+      xv = to_f32(rx[P]);
     }
-    float d2 = softplus_log2e(fmaf(to_f32(rdt), kLog2e, bias2));
+    float d2 = softplus_log2e(fmaf(to_f32(rdt[P]), kLog2e, bias2));
     if constexpr (!STEADY) {   // a padded step is the identity: Delta = 0, x = 0
       const bool lv = c * T + w < seg_n;
       d2 = lv ? d2 : 0.f;
@@ -315,13 +319,13 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
     if (bcwave && bclane) {
       const int t = bcrow0 + bcj;
       if (w < 8)
-        s_b[P][bcn][t] = STRUCT ? to_f32(rbc) * ra : to_f32(rbc);
+        s_b[P][bcn][t] = STRUCT ? to_f32(rbc[P]) * ra : to_f32(rbc[P]);
       else if constexpr (OUT)
-        s_c[P][bcn][t] = to_f32(rbc);
+        s_c[P][bcn][t] = to_f32(rbc[P]);
     }
     if constexpr (OUT) {
       if (hasZ)
-        eg[P] = silu(to_f32(rz));
+        eg[P] = silu(to_f32(rz[P]));
       else
         eg[P] = 1.f;
       ed[P] = dsk * xv;
@@ -382,7 +386,7 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
     }
     if (STEADY || c + 1 < nchunks) {
       prologue(Par<Q>{}, steadyc, c + 1);
-      if (STEADY || c + 2 < nchunks) gload(steadyc, c + 2);
+      if (STEADY || c + 3 < nchunks) gload(Par<Q>{}, steadyc, c + 3);
     }
     if (STEADY || c >= 1) {
       epilogue(Par<Q>{}, c - 1, pg, pd);
@@ -461,15 +465,16 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
   }
   __syncthreads();
   if (nchunks > 0) {
-    gload(std::false_type{}, 0);
+    gload(Par<0>{}, std::false_type{}, 0);
     prologue(Par<0>{}, std::false_type{}, 0);
-    if (nchunks > 1) gload(std::false_type{}, 1);
+    if (nchunks > 1) gload(Par<1>{}, std::false_type{}, 1);
+    if (nchunks > 2) gload(Par<0>{}, std::false_type{}, 2);
     __syncthreads();
     iteration(Par<0>{}, std::false_type{}, 0);
-    // steady iterations: c >= 1 and chunks c + 1, c + 2 full (pairs, so the LDS
-    // buffer index stays a compile-time constant)
+    // steady iterations: c >= 1 and chunks c + 1 .. c + 3 full (pairs, so the LDS
+    // buffer and load register set indices stay compile-time constants)
     int c = 1;
-    for (; c + 3 < nfull; c += 2) {
+    for (; c + 4 < nfull; c += 2) {
       iteration(Par<1>{}, std::true_type{}, c);
       iteration(Par<0>{}, std::true_type{}, c + 1);
     }
