@@ -549,7 +549,11 @@ int bwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dty
     float* carry = sw;
     p.agg_h = sw + lo.nseg * bdn;
     p.agg_s = sw + 2 * lo.nseg * bdn;
+    // the aggregate pass with two states per wave (two workgroups share a CU); the
+    // checkpoint pass itself runs the row layout
+    p.npw = N >= 3 ? 2 : 1;
     e = sscan::launch_fwd_aggregate(p, bf16, s);
+    p.npw = 1;
     if (e != hipSuccess) return hip_fail(e, "segment aggregate launch");
     e = sscan::launch_fwd_carry(p.agg_h, p.agg_s, A, initial_state, carry, batch, dim, static_cast<int>(N),
                                 lo.nseg, s);

@@ -831,11 +831,26 @@ __global__ __launch_bounds__(256) void bwd_carry_kernel(const float* __restrict_
   const int64_t d = bd % dim;
   const float a = A[d * N + n];
   float g = dlast ? dlast[i] : 0.f;
-  for (int s = nseg - 1; s >= 0; --s) {
-    gin[static_cast<int64_t>(s) * total + i] = g;
-    if (s > 0)
-      g = fmaf(hw_exp2(a * ragg_s[static_cast<int64_t>(s) * batch * dim + bd]), g,
-               ragg_g[static_cast<int64_t>(s) * total + i]);
+  // segments in groups of G, right to left: a group's aggregates are loaded together,
+  // so their latencies overlap instead of adding up along the sequential combine
+  constexpr int G = 8;
+  for (int s0 = nseg - 1; s0 >= 0; s0 -= G) {
+    float gv[G], sv[G];
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      const int s = s0 - k;
+      const bool have = s > 0;   // the first segment has no aggregate
+      gv[k] = have ? ragg_g[static_cast<int64_t>(s) * total + i] : 0.f;
+      sv[k] = have ? ragg_s[static_cast<int64_t>(s) * batch * dim + bd] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      const int s = s0 - k;
+      if (s >= 0) {
+        gin[static_cast<int64_t>(s) * total + i] = g;
+        g = fmaf(hw_exp2(a * sv[k]), g, gv[k]);
+      }
+    }
   }
 }
 
@@ -871,14 +886,34 @@ __global__ __launch_bounds__(256) void bwd_reduce_params(const float* __restrict
   if (i >= dim * N) return;
   const int n = static_cast<int>(i / dim);
   const int64_t d = i - static_cast<int64_t>(n) * dim;
+  // rows in groups of G, loaded together and then added in row order (the same
+  // order as one at a time, so the sums are unchanged)
+  constexpr int G = 8;
   float s = 0.f;
-  for (int64_t r = 0; r < rows; ++r) s += gAp[r * N * dim + i];
+  for (int64_t r0 = 0; r0 < rows; r0 += G) {
+    float v[G];
+#pragma unroll
+    for (int k = 0; k < G; ++k) v[k] = (r0 + k < rows) ? gAp[(r0 + k) * N * dim + i] : 0.f;
+#pragma unroll
+    for (int k = 0; k < G; ++k)
+      if (r0 + k < rows) s += v[k];
+  }
   dA[d * N + n] = s;
   if (n == 0) {
     float sD = 0.f, sb = 0.f;
-    for (int64_t r = 0; r < rows; ++r) {
-      sD += gDp[r * dim + d];
-      sb += gbp[r * dim + d];
+    for (int64_t r0 = 0; r0 < rows; r0 += G) {
+      float vD[G], vb[G];
+#pragma unroll
+      for (int k = 0; k < G; ++k) {
+        vD[k] = (r0 + k < rows) ? gDp[(r0 + k) * dim + d] : 0.f;
+        vb[k] = (r0 + k < rows) ? gbp[(r0 + k) * dim + d] : 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < G; ++k)
+        if (r0 + k < rows) {
+          sD += vD[k];
+          sb += vb[k];
+        }
     }
     if (dD) dD[d] = sD;
     if (dbias) dbias[d] = sb;
