@@ -137,6 +137,15 @@ sscan_status sscan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstat
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Workspace bytes that give sscan_fwd_segmented the split it asks for: num_segments
+ * after the same clamping the call applies (to whole 16-step chunks of seqlen and at
+ * least one segment).  num_segments == 0 gives sscan_fwd_workspace_size.  Returns 0
+ * when that plan has one segment, or for a negative num_segments or an invalid shape.
+ */
+size_t sscan_fwd_segmented_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                          int dtype, int64_t num_segments);
+
+/*
  * Same as sscan_fwd, with the number of sequence segments chosen by the caller
  * (num_segments >= 1; it is clamped to what the workspace and seqlen allow).
  * num_segments == 0 means "choose automatically" and equals sscan_fwd.

@@ -32,6 +32,8 @@ _lib.sscan_last_error.argtypes = []
 _lib.sscan_last_error.restype = ctypes.c_char_p
 _lib.sscan_fwd_workspace_size.argtypes = [_I64, _I64, _I64, _I64, ctypes.c_int]
 _lib.sscan_fwd_workspace_size.restype = _SZ
+_lib.sscan_fwd_segmented_workspace_size.argtypes = [_I64, _I64, _I64, _I64, ctypes.c_int, _I64]
+_lib.sscan_fwd_segmented_workspace_size.restype = _SZ
 _U32 = ctypes.c_uint
 _lib.sscan_fwd.argtypes = [_I64, _I64, _I64, _I64, ctypes.c_int, _U32] + [_P] * 11 + [_P, _SZ, _P]
 _lib.sscan_fwd.restype = ctypes.c_int
@@ -110,7 +112,11 @@ def _stream(dev) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
-def fwd_workspace_size(batch: int, seqlen: int, dim: int, dstate: int, dtype=torch.bfloat16) -> int:
+def fwd_workspace_size(batch: int, seqlen: int, dim: int, dstate: int, dtype=torch.bfloat16,
+                       num_segments: Optional[int] = None) -> int:
+    """Workspace bytes for the automatic split, or for num_segments segments."""
+    if num_segments is not None:
+        return int(_lib.sscan_fwd_segmented_workspace_size(batch, seqlen, dim, dstate, _DTYPES[dtype], num_segments))
     return int(_lib.sscan_fwd_workspace_size(batch, seqlen, dim, dstate, _DTYPES[dtype]))
 
 
@@ -160,9 +166,7 @@ def sscan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Te
     if ls is not None:
         _dev(ls, "last_state", torch.float32, (batch, dim, dstate))
     if workspace is None:
-        need = fwd_workspace_size(batch, seqlen, dim, dstate, x.dtype)
-        if num_segments is not None and num_segments > 1:
-            need = max(need, 4 * num_segments * batch * dim * (2 * dstate + 1))
+        need = fwd_workspace_size(batch, seqlen, dim, dstate, x.dtype, num_segments)
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device) if need > 0 else None
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     flags = (SSCAN_FLAG_EULER if euler else 0) | (SSCAN_FLAG_STRUCTURED_A if structured_a else 0)

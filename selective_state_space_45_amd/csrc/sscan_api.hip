@@ -648,6 +648,14 @@ size_t sscan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int6
   return seg_workspace_bytes(batch, dim, dstate, pl.nseg);
 }
 
+size_t sscan_fwd_segmented_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+                                          int64_t num_segments) {
+  (void)dtype;
+  if (batch <= 0 || seqlen <= 0 || dim <= 0 || dstate < 1 || dstate > SSCAN_MAX_DSTATE || num_segments < 0) return 0;
+  const SegPlan pl = plan_segments(batch, seqlen, dim, dstate, num_segments, ~size_t(0), true);
+  return seg_workspace_bytes(batch, dim, dstate, pl.nseg);
+}
+
 sscan_status sscan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype, unsigned int flags,
                        const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
                        const void* z, const float* delta_bias, const float* initial_state, void* y, float* last_state,

@@ -24,6 +24,8 @@ def lib():
     lb.sscan_last_error.restype = ctypes.c_char_p
     lb.sscan_fwd_workspace_size.argtypes = [I64, I64, I64, I64, ctypes.c_int]
     lb.sscan_fwd_workspace_size.restype = SZ
+    lb.sscan_fwd_segmented_workspace_size.argtypes = [I64, I64, I64, I64, ctypes.c_int, I64]
+    lb.sscan_fwd_segmented_workspace_size.restype = SZ
     lb.sscan_bwd_workspace_size.argtypes = [I64, I64, I64, I64, ctypes.c_int]
     lb.sscan_bwd_workspace_size.restype = SZ
     lb.sscan_bwd.argtypes = [I64, I64, I64, I64, ctypes.c_int, U32] + [P] * 21 + [SZ, P]
@@ -157,6 +159,23 @@ def test_workspace_size(lib):
     # batch 6, dim 1536, seqlen 65536: 144 workgroups x 32 segments = 9 full rounds
     assert lib.sscan_fwd_workspace_size(6, 65536, 1536, 16, 1) == 32 * 4 * 6 * 1536 * 33
     assert lib.sscan_fwd_workspace_size(1, 0, 2560, 16, 1) == 0
+
+
+def test_segmented_workspace_size(lib):
+    per_seg = 4 * 2 * 1536 * 33   # carry + end state + step sum, fp32, per segment
+    f = lib.sscan_fwd_segmented_workspace_size
+    # num_segments == 0 is the automatic plan
+    assert f(2, 2048, 1536, 16, 0, 0) == lib.sscan_fwd_workspace_size(2, 2048, 1536, 16, 0)
+    assert f(2, 2048, 1536, 16, 0, 3) == 3 * per_seg
+    assert f(2, 2048, 1536, 16, 0, 1) == 0           # one segment: no split
+    # clamped to whole 16-step chunks: 100 steps hold 7 chunks
+    assert f(2, 100, 1536, 16, 0, 50) == 7 * per_seg
+    # 1000 steps asked in 9 segments: 112-step segments, so 9 of them
+    assert f(2, 1000, 1536, 16, 0, 9) == 9 * per_seg
+    # 7 segments of 1000 steps round to 144 steps each, which 7 segments cover
+    assert f(2, 1000, 1536, 16, 0, 7) == 7 * per_seg
+    assert f(2, 2048, 1536, 16, 0, -1) == 0
+    assert f(2, 2048, 1536, 17, 0, 3) == 0
 
 
 def bwd(lib, batch=2, L=8, dim=4, N=4, dtype=0, flags=0, z=None, dz=None, D=None, dD=None, ws=None, wsb=0,
