@@ -183,6 +183,18 @@ def test_forced_segments(ss, orc, dtype, segs):
     check_workload(ss, orc, w, num_segments=segs, label=f"segments={segs}")
 
 
+@pytest.mark.parametrize("shape", [(1, 2048, 1536, "f32"), (4, 2048, 1536, "f32"), (2, 1000, 1536, "bf16"),
+                                   (1, 4096, 640, "bf16")])
+def test_automatic_split_plans(ss, orc, shape):
+    # grids of 10 to 96 (batch, tile) workgroups, so the forward splits the sequence with
+    # the segment count of its round cost model (19, 5, 9 and 43 segments here; the
+    # last with segments of 96 steps), against the oracle over every output
+    b, L, D, dtype = shape
+    w = W.make_scan_inputs(b, L, D, 16, dtype, seed=21 + b, name="automatic split")
+    h0 = np.random.default_rng(22).standard_normal((b, D, 16)).astype(np.float32)
+    check_workload(ss, orc, w, h0=h0, label=f"automatic split B={b} L={L} D={D} {dtype}")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_optional_inputs_absent(ss, orc, dtype):
     w = W.make_scan_inputs(1, 70, 64, 16, dtype, seed=9, with_z=False, with_D=False, with_bias=False,
