@@ -42,21 +42,25 @@
 
 namespace sscan {
 
-// Sum over the 16 lanes of each row of p[t], t = 0..15, scattered: lane t of the row
-// ends with the row's sum for timestep t.  Four halvings; each pairs every lane with a
-// partner in the other half of its group and keeps the half of the timesteps its own
-// lane bit selects:
-//   bit 3: partner lane ^ 8 (row_ror:8); lanes 0-7 keep t < 8.  Each output register
-//          is written by two adds masked to lane groups of four (bank_mask), one per
-//          half, so no selects are needed.
-//   bit 2: partner lane ^ 7 within each half row (row_half_mirror); masked the same way.
-//   bit 1, bit 0: partner lane ^ 2, ^ 1 (quad permutes); the kept and sent values are
-//          chosen per lane with selects.
-// The masked adds are written as inline assembly (the compiler has no masked-add
-// builtin); each block starts with the two wait states that a DPP read of a VGPR
-// written by the preceding VALU instruction requires.  All 64 lanes must be active.
-__device__ __forceinline__ float row_reduce_scatter16(const float (&p)[16], int lane) {
-  float q[8], r[4];
+// Partial sums over the 16 lanes of each row of p[t], t = 0..15.  Two halvings; each
+// pairs every lane with a partner in another group of four lanes and keeps the half
+// of the timesteps its own lane bit selects:
+//   bit 3: partner lane ^ 8 (row_ror:8); lanes 0-7 keep t < 8;
+//   bit 2: partner lane ^ 7 within each half row (row_half_mirror); lanes 0-3 and
+//          8-11 keep the lower four of their eight timesteps.
+// Each output register is written by two adds masked to lane groups of four
+// (bank_mask), one per half, so no selects are needed.  Afterwards lane l of a row
+// (group k = l >> 2) holds in r[j] a partial sum for timestep 4k + j over four of the
+// row's lanes ({l, l ^ 8, 7 - l, (7 - l) ^ 8} within the half rows); the four lanes of
+// group k together cover all 16, and the epilogue adds their four partials.  (The two
+// remaining halvings of a full reduce-scatter pair lanes inside a group of four, where
+// bank masks cannot separate them; with per-lane selects they cost 9 VALU per chunk
+// against the epilogue's 3 adds.)  The masked adds are written as inline assembly
+// (the compiler has no masked-add builtin); each block starts with the two wait states
+// that a DPP read of a VGPR written by the preceding VALU instruction requires.  All
+// 64 lanes must be active.
+__device__ __forceinline__ void row_reduce_partial16(const float (&p)[16], float (&r)[4]) {
+  float q[8];
   asm("s_nop 1\n\t"
       "v_add_f32_dpp %0, %4, %4 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
       "v_add_f32_dpp %0, %8, %8 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
@@ -90,17 +94,6 @@ __device__ __forceinline__ float row_reduce_scatter16(const float (&p)[16], int 
       "v_add_f32_dpp %3, %11, %11 row_half_mirror row_mask:0xf bank_mask:0xa"
       : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
       : "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]), "v"(q[4]), "v"(q[5]), "v"(q[6]), "v"(q[7]));
-  const bool b1 = (lane & 2) != 0, b0 = (lane & 1) != 0;
-  float s[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const float keep = b1 ? r[j + 2] : r[j];
-    const float send = b1 ? r[j] : r[j + 2];
-    s[j] = keep + dpp_move<0x4E>(send);   // quad_perm [2,3,0,1]
-  }
-  const float keep = b0 ? s[1] : s[0];
-  const float send = b0 ? s[0] : s[1];
-  return keep + dpp_move<0xB1>(send);     // quad_perm [1,0,3,2]
 }
 
 // One workgroup: (batch row b, 64-channel tile, segment); 16 waves x 4 channels x 16
@@ -146,7 +139,12 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
   __shared__ float2 s_dx[2][T][DP];
   __shared__ __align__(16) float s_b[2][16][BR];
   __shared__ __align__(16) float s_c[OUT ? 2 : 1][16][BR];
-  __shared__ float s_y[OUT ? 2 : 1][T][YP];
+  // readout partials [k][j][i][column]: lane i of group k's partial for timestep 4k + j
+  // of channel ch, at column ch + 2 (4k + i).  Rows of 96 words; the column shift puts
+  // a half wave's stores (channels 4w, 4w + 1, all k and i) and the epilogue's reads
+  // (64 channels) on distinct banks.
+  constexpr int YR = kTile + 32;
+  __shared__ float s_yp[OUT ? 2 : 1][4][4][4][YR];
   // checkpoint states of a chunk's two blocks, [half][state][channel], so that they
   // leave as whole rows of 64 channels (the layout the backward pass reads)
   __shared__ float s_ck[CKPT ? 2 : 1][2][16][YP];
@@ -336,7 +334,9 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
     if constexpr (OUT) {
       const int l = c * T + w;
       if (l < seg_n && dvalid) {
-        const float v = s_y[P][w][lane];
+        // the four partials of timestep w (group k = w / 4, j = w % 4) of this channel
+        const float* src = &s_yp[P][w >> 2][w & 3][0][lane + 8 * (w >> 2)];
+        const float v = (src[0] + src[YR + 2]) + (src[2 * YR + 4] + src[3 * YR + 6]);
         store_val(at_off(Yb + static_cast<int64_t>(l) * dim, static_cast<unsigned>(lane) * sizeof(Tin)), (v + dx) * g);
       }
     }
@@ -454,7 +454,14 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
         if constexpr (OUT) p[t] = cb[t >> 2][t & 3] * h;
       });
     }
-    if constexpr (OUT) s_y[P][ln][cr] = row_reduce_scatter16(p, lane);
+    if constexpr (OUT) {
+      float r[4];
+      row_reduce_partial16(p, r);
+      const int k = ln >> 2, i = ln & 3;
+      float* dst = &s_yp[P][k][0][i][cr + 2 * (4 * k + i)];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dst[j * 4 * YR] = r[j];
+    }
     __syncthreads();
   };
 
