@@ -100,6 +100,36 @@ __device__ __forceinline__ void lane_reduce32(float* v, int lane) {
   v[0] += dpp<kDppQuadXor1>(v[0]);
 }
 
+// The halvings through row_ror:8 (partner lane ^ 8) and row_half_mirror (partner
+// ^ 7 within each half row) pair lanes in different groups of four, so each output
+// register is written by two adds masked to lane groups (bank_mask), one per half,
+// with no per-lane selects: 2 VALU per output instead of 3.  Lanes with the bit clear
+// keep the lower half of the elements, as halve_dpp does.  Inline assembly (the
+// compiler has no masked-add builtin); each block starts with the two wait states a
+// DPP read of a VGPR written by the preceding VALU instruction requires.  All 64
+// lanes must be active.
+__device__ __forceinline__ void halve_ror8_2(float* v) {
+  float o0, o1;
+  asm("s_nop 1\n\t"
+      "v_add_f32_dpp %0, %2, %2 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %0, %4, %4 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %1, %3, %3 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %1, %5, %5 row_ror:8 row_mask:0xf bank_mask:0xc"
+      : "=&v"(o0), "=&v"(o1)
+      : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]));
+  v[0] = o0;
+  v[1] = o1;
+}
+__device__ __forceinline__ void halve_mirror_1(float* v) {
+  float o0;
+  asm("s_nop 1\n\t"
+      "v_add_f32_dpp %0, %1, %1 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
+      "v_add_f32_dpp %0, %2, %2 row_half_mirror row_mask:0xf bank_mask:0xa"
+      : "=&v"(o0)
+      : "v"(v[0]), "v"(v[1]));
+  v[0] = o0;
+}
+
 // Sum of v[0..15] over the 64 lanes of a wave, as a reduce-scatter: afterwards lane
 // L holds in v[0] the total of element L >> 2 (all four lanes of a quad agree).
 __device__ __forceinline__ void lane_reduce16(float* v, int lane) {
@@ -113,8 +143,9 @@ __device__ __forceinline__ void lane_reduce16(float* v, int lane) {
     const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[k]), __float_as_uint(v[k + 4]), false, false);
     v[k] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
   }
-  halve_dpp<kDppRowRor8, 8, 2>(v, lane);
-  halve_dpp<kDppRowHalfMirror, 4, 1>(v, lane);
+  (void)lane;
+  halve_ror8_2(v);
+  halve_mirror_1(v);
   v[0] += dpp<kDppQuadXor2>(v[0]);
   v[0] += dpp<kDppQuadXor1>(v[0]);
 }
