@@ -6,6 +6,11 @@ batch of the training-shape workload: batch 8, seqlen 4096, dim 2048, dstate 16,
 bf16 x/delta/z/B/C/y, fp32 A/D/bias/state.  Inputs are resident in HBM before the
 timed region.  One JSON line is printed.
 
+Every timed phase starts after untimed back-to-back calls (0.25 s before the warmup
+steps, 0.1 s before each other leg): under sustained load the GPU's clocks rise over
+the first tens of milliseconds, and a kernel trace showed the forward's launch time
+falling from 0.48 to 0.37 ms over that stretch.
+
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
                     [--no-euler] [--no-structured] [--no-bwd] [--no-conv] [--copy-calibration]
     python bench.py --summarize-counters FETCH_CSV WRITE_CSV   (CPU only)
@@ -148,10 +153,11 @@ def per_config_report() -> None:
     flush = Flush(torch, dev)
 
     def median_ms(fn, n=50, warm=3):
-        # median of n launches, each after a write that evicts L2 and the MALL
+        # median of n launches, each after a write that evicts L2 and the MALL, once
+        # back-to-back calls have settled the clocks
         for _ in range(warm):
             fn()
-        torch.cuda.synchronize()
+        settle(torch, fn, 0.1)
         return timed_median(torch, fn, n, flush)[0]
 
     for name in ("tiny", "mamba130m_layer", "train_shape", "long_context"):
@@ -227,6 +233,22 @@ def per_config_report() -> None:
                       "hbm_frac": round(nb / (ms * 1e-3) / 1e9 / 8000, 4), "oracle_s_per_step": round(cpu_s, 4),
                       "oracle_threads": oracle.last_threads_used(),
                       "note": "errors over 1000 steps are checked by the parity tests"}), flush=True)
+
+
+SETTLE_S = 0.25
+
+
+def settle(torch, fn, seconds=SETTLE_S, max_steps=4000):
+    """Run fn back to back (in groups of 10, synchronizing after each group) for about
+    `seconds`, untimed; returns the number of calls."""
+    t_end = time.perf_counter() + seconds
+    n = 0
+    while time.perf_counter() < t_end and n < max_steps:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        n += 10
+    return n
 
 
 class Flush:
@@ -332,6 +354,11 @@ def main():
     def step():
         ss.sscan_fwd(x, dt, A, B, C, D=D, z=z, delta_bias=bias, out=y, last_state=st, workspace=ws)
 
+    # untimed clock settling, then the W warmup steps: under sustained load the GPU's
+    # clocks rise over the first tens of milliseconds (in a kernel trace the forward's
+    # back-to-back launch times fell from 0.48 to 0.37 ms over the first 30 ms), so the
+    # step runs back to back for SETTLE_S seconds before anything is timed
+    settle_steps = settle(torch, step)
     # the timed region: K back-to-back steps, inputs resident in HBM
     for _ in range(args.warmup):
         step()
@@ -351,6 +378,7 @@ def main():
     # the dominant kernel on its own: median of flushed launches (one sscan_fwd call is
     # one kernel launch on this shape)
     nruns = max(50, args.kernel_runs)
+    settle(torch, step, 0.1)
     kern_ms, kern_mean = timed_median(torch, step, nruns, flush)
     roof = roofline_entry(nbytes, ops, kern_ms, "fwd_row_kernel<bf16, output mode, N=16, zero-order hold>",
                           f"median of {nruns} launches, HIP events on the launch stream, each after a "
@@ -358,9 +386,7 @@ def main():
     roof["kernel_ms_mean"] = round(kern_mean, 5)
 
     def leg_ms(fn, n):
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
+        settle(torch, fn, 0.1)
         return timed_median(torch, fn, n, flush)[0]
 
     # the structured-A path (SSCAN_FLAG_STRUCTURED_A) on the same workload, whose
@@ -459,8 +485,7 @@ def main():
         with torch.cuda.graph(g):
             for i in range(per_graph):
                 ss.sscan_step(states[i % nstates], tx, tdt, dA, tB, tC, D=dD, z=tz, out=yd)
-        g.replay()
-        torch.cuda.synchronize()
+        settle(torch, g.replay, 0.1)
         reps = max(1, args.decode_steps // per_graph)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -521,6 +546,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_settle": {"steps": settle_steps, "seconds": SETTLE_S,
+                         "note": "untimed back-to-back steps before the warmup steps"},
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
