@@ -9,7 +9,11 @@ timed region.  One JSON line is printed.
 Every timed phase starts after untimed back-to-back calls (0.25 s before the warmup
 steps, 0.1 s before each other leg): under sustained load the GPU's clocks rise over
 the first tens of milliseconds, and a kernel trace showed the forward's launch time
-falling from 0.48 to 0.37 ms over that stretch.
+falling from 0.48 to 0.37 ms over that stretch.  Flushed medians (each launch after a
+1 GiB write) are taken after as many untimed flushed launches, since the alternation
+with the memory-bound flush moves the clocks again.  roofline.achieved is the timed
+region's average launch (HIP events around the K steps; one launch per step), which
+is what a kernel trace of the same run averages; roofline.flushed holds the median.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
                     [--no-euler] [--no-structured] [--no-bwd] [--no-conv] [--copy-calibration]
@@ -158,6 +162,10 @@ def per_config_report() -> None:
         for _ in range(warm):
             fn()
         settle(torch, fn, 0.1)
+        for _ in range(n):
+            flush()
+            fn()
+        torch.cuda.synchronize()
         return timed_median(torch, fn, n, flush)[0]
 
     for name in ("tiny", "mamba130m_layer", "train_shape", "long_context"):
@@ -363,12 +371,17 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    ev0.record()
     for _ in range(args.steps):
         step()
+    ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
+    # the same region on the launch stream (HIP events): one kernel launch per step here
+    region_ms = ev0.elapsed_time(ev1) / args.steps
 
     nbytes = W.fwd_algorithmic_bytes(w.batch, w.seqlen, w.dim, w.dstate, "bf16")
     value = nbytes / (ms_per_step * 1e-3) / 1e9
@@ -377,16 +390,34 @@ def main():
 
     # the dominant kernel on its own: median of flushed launches (one sscan_fwd call is
     # one kernel launch on this shape)
+    # roofline: the timed region's average launch (HIP events on the launch stream);
+    # beside it the median of individually timed launches, each after a cache flush,
+    # taken after as many untimed flushed launches (the alternation of the memory-bound
+    # flush and the kernel moves the clocks again: in a trace the flushed launches fell
+    # from 0.45 to 0.37 ms over their first 60)
     nruns = max(50, args.kernel_runs)
-    settle(torch, step, 0.1)
+    for _ in range(nruns):
+        flush()
+        step()
+    torch.cuda.synchronize()
     kern_ms, kern_mean = timed_median(torch, step, nruns, flush)
-    roof = roofline_entry(nbytes, ops, kern_ms, "fwd_row_kernel<bf16, output mode, N=16, zero-order hold>",
-                          f"median of {nruns} launches, HIP events on the launch stream, each after a "
-                          f"{FLUSH_BYTES >> 20} MiB write that evicts L2 and MALL")
-    roof["kernel_ms_mean"] = round(kern_mean, 5)
+    roof = roofline_entry(nbytes, ops, region_ms, "fwd_row_kernel<bf16, output mode, N=16, zero-order hold>",
+                          f"average over the {args.steps} back-to-back launches of the timed region, HIP events "
+                          "on the launch stream (one launch per step)")
+    roof["flushed"] = {"kernel_ms": round(kern_ms, 5), "kernel_ms_mean": round(kern_mean, 5),
+                       "achieved": round(nbytes / (kern_ms * 1e-3) / 1e9, 2),
+                       "frac": round(nbytes / (kern_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                       "timing": f"median of {nruns} launches, HIP events on the launch stream, each after a "
+                                 f"{FLUSH_BYTES >> 20} MiB write that evicts L2 and MALL (after {nruns} "
+                                 "untimed ones)"}
 
     def leg_ms(fn, n):
+        # as the flushed figure above: settled, then n untimed flushed launches first
         settle(torch, fn, 0.1)
+        for _ in range(n):
+            flush()
+            fn()
+        torch.cuda.synchronize()
         return timed_median(torch, fn, n, flush)[0]
 
     # the structured-A path (SSCAN_FLAG_STRUCTURED_A) on the same workload, whose
