@@ -958,18 +958,20 @@ void launch_bwd_one(const BwdParams& p, hipStream_t s) {
   BwdShape sh{p.batch, p.L, p.dim, p.ndtiles, p.nblk, p.seg_blocks, p.N, p.nseg};
   if (p.nseg > 1) {
     const dim3 agrid(static_cast<unsigned>(p.ndtiles * p.batch * (p.nseg - 1)));
-    if constexpr (NF == 16) {
-      hipLaunchKernelGGL((bwd_agg_row_kernel<Tin>), agrid, dim3(1024), 0, s, static_cast<const Tin*>(p.dt),
-                         static_cast<const Tin*>(p.z), static_cast<const Tin*>(p.C), static_cast<const Tin*>(p.dy),
-                         p.A, p.bias, p.ragg_g, p.ragg_s, sh);
-    } else {
-      // one state per wave in the aggregate pass: twice the reverse pass's waves, for
-      // occupancy (measured: two states per wave was no faster on the training shape)
-      constexpr int AS = 1;
-      constexpr int AW = NW * kBwdSpw / AS;
-      hipLaunchKernelGGL((bwd_agg_kernel<Tin, AW, AS, NF>), agrid, dim3(AW * 64), 0, s, static_cast<const Tin*>(p.dt),
-                         static_cast<const Tin*>(p.z), static_cast<const Tin*>(p.C), static_cast<const Tin*>(p.dy),
-                         p.A, p.bias, p.ragg_g, p.ragg_s, sh);
+    if (!p.agg_done) {   // else formed by the checkpoint pass
+      if constexpr (NF == 16) {
+        hipLaunchKernelGGL((bwd_agg_row_kernel<Tin>), agrid, dim3(1024), 0, s, static_cast<const Tin*>(p.dt),
+                           static_cast<const Tin*>(p.z), static_cast<const Tin*>(p.C), static_cast<const Tin*>(p.dy),
+                           p.A, p.bias, p.ragg_g, p.ragg_s, sh);
+      } else {
+        // one state per wave in the aggregate pass: twice the reverse pass's waves, for
+        // occupancy (measured: two states per wave was no faster on the training shape)
+        constexpr int AS = 1;
+        constexpr int AW = NW * kBwdSpw / AS;
+        hipLaunchKernelGGL((bwd_agg_kernel<Tin, AW, AS, NF>), agrid, dim3(AW * 64), 0, s,
+                           static_cast<const Tin*>(p.dt), static_cast<const Tin*>(p.z), static_cast<const Tin*>(p.C),
+                           static_cast<const Tin*>(p.dy), p.A, p.bias, p.ragg_g, p.ragg_s, sh);
+      }
     }
     const int64_t total = p.batch * p.dim * p.N;
     hipLaunchKernelGGL(bwd_carry_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s,

@@ -26,6 +26,8 @@ extern template hipError_t launch_fwd_row<kFwdOutCkpt, true>(const FwdParams&, b
 extern template hipError_t launch_fwd_row<kFwdOutConv, false>(const FwdParams&, bool, hipStream_t);
 extern template hipError_t launch_fwd_row<kFwdOutConv, true>(const FwdParams&, bool, hipStream_t);
 extern template hipError_t launch_fwd_row<kFwdOut, false, true>(const FwdParams&, bool, hipStream_t);
+extern template hipError_t launch_fwd_row<kFwdCkptAgg, false>(const FwdParams&, bool, hipStream_t);
+extern template hipError_t launch_fwd_row<kFwdCkptAgg, true>(const FwdParams&, bool, hipStream_t);
 
 // carry[s] = state entering segment s: carry[0] = h_init (or 0),
 // carry[s+1] = exp2(A * S_s) * carry[s] + hend_s, where S_s is the segment's sum of
@@ -159,6 +161,10 @@ hipError_t launch_fwd_aggregate(const FwdParams& p, bool bf16, hipStream_t s) {
 
 hipError_t launch_fwd_checkpoints(const FwdParams& p, bool bf16, hipStream_t s) {
   return launch_fwd_mode<kFwdCkpt>(p, bf16, s);
+}
+
+hipError_t launch_fwd_checkpoints_agg(const FwdParams& p, bool bf16, hipStream_t s) {
+  return p.euler ? launch_fwd_row<kFwdCkptAgg, true>(p, bf16, s) : launch_fwd_row<kFwdCkptAgg, false>(p, bf16, s);
 }
 
 hipError_t launch_fwd_carry(const float* agg_h, const float* agg_s, const float* A, const float* h_init, float* carry,

@@ -609,7 +609,7 @@ __global__ __launch_bounds__(NSPLIT * 64) void fwd_kernel(
 
 template <typename Tin, int NS, int NPW, int MODE, bool PR, int NF, bool EU, bool CV>
 void launch_one(const FwdParams& p, dim3 grid, hipStream_t s) {
-  FwdShape sh{p.batch, p.L, p.dim, p.seg_len, p.ndtiles, p.nblk, p.N, p.nseg, p.dconv};
+  FwdShape sh{p.batch, p.L, p.dim, p.seg_len, p.ndtiles, p.nblk, p.rseg_len, p.N, p.nseg, p.dconv};
   hipLaunchKernelGGL((fwd_kernel<Tin, NS, NPW, MODE, PR, NF, EU, CV>), grid, dim3(NS * 64), 0, s,
                      static_cast<const Tin*>(p.x), static_cast<const Tin*>(p.dt), static_cast<const Tin*>(p.z),
                      static_cast<const Tin*>(p.B), static_cast<const Tin*>(p.C), p.A, p.Dskip, p.bias, p.h_init,

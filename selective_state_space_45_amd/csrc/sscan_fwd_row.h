@@ -99,6 +99,8 @@ __device__ __forceinline__ void row_reduce_partial16(const float (&p)[16], float
 // One workgroup: (batch row b, 64-channel tile, segment); 16 waves x 4 channels x 16
 // states.  MODE: kFwdOut (y and the final state), kFwdCkpt (no y: the state entering
 // every block of kBwdBlock steps, for the backward pass), kFwdOutCkpt (both),
+// kFwdCkptAgg (kFwdCkpt, and in the same sweep the reverse aggregates of the backward
+// pass's sequence segments after the first: see the adjoint note below),
 // kFwdOutConv (kFwdOut on the output of the convolution prologue: x is the raw input
 // of a causal depthwise conv1d over time, conv_w [dim][dconv] taps and optional
 // conv_b [dim], followed by SiLU, as in the page-3 report's MambaBlock (section 3,
@@ -111,17 +113,35 @@ __device__ __forceinline__ void row_reduce_partial16(const float (&p)[16], float
 // the prologue stages x / c_d with Delta and B / a_n with B (both shared work), and each
 // step forms k with one multiply instead of two.  The workgroup verifies the form on its
 // tile exactly and takes the plain staging where it does not hold.
+//
+// Adjoint note (kFwdCkptAgg).  The backward pass runs the adjoint recurrence
+// g_{t-1} = Abar_t (g_t + C_t gy_t) from the sequence end (gy = dy silu(z): the
+// gradient of y before the D term; page-3 report section 4.1, the reverse scan of the
+// backward pass).  Cut into two segments, the first rseg_len steps and the rest, the
+// second segment's map from the gradient at the sequence end to the gradient at its
+// start is g -> P g + G with P = prod_t Abar_t (as exp2(A sum_t Delta log2(e)), from
+// the staged sum) and G = sum_t (prod_{s <= t} Abar_s) C_t gy_t, products from the
+// segment's first step.  G is a sum over the segment in any order; here it is
+// accumulated forward, during the checkpoint sweep that already forms every Abar_t: a
+// running product pr <- pr Abar_t and G <- G + pr C_t gy_t, three VALU per state and
+// step, instead of a separate reverse sweep that recomputes Delta and Abar.  One
+// forward segment (the sweep starts at position 0); rseg_len is a multiple of kChunk,
+// so the second segment starts at a chunk start and ends with the last chunk.
 template <typename Tin, int MODE, int NFIX, bool EULER, bool STRUCT = false>
 __global__ __launch_bounds__(1024) void fwd_row_kernel(
     const Tin* __restrict__ xg, const Tin* __restrict__ dtg, const Tin* __restrict__ zg,
     const Tin* __restrict__ Bg, const Tin* __restrict__ Cg, const float* __restrict__ Ag,
     const float* __restrict__ Dg, const float* __restrict__ biasg, const float* __restrict__ h_init,
     Tin* __restrict__ yg, float* __restrict__ h_last, float* __restrict__ ckpt, const float* __restrict__ conv_w,
-    const float* __restrict__ conv_b, const float* __restrict__ conv_s, FwdShape sh) {
+    const float* __restrict__ conv_b, const float* __restrict__ conv_s, const Tin* __restrict__ dyg,
+    float* __restrict__ ragg_g, float* __restrict__ ragg_s, FwdShape sh) {
   constexpr bool CONV = MODE == kFwdOutConv;
   constexpr bool OUT = MODE == kFwdOut || MODE == kFwdOutCkpt || CONV;
-  constexpr bool CKPT = MODE == kFwdCkpt || MODE == kFwdOutCkpt;
+  constexpr bool AGG = MODE == kFwdCkptAgg;
+  constexpr bool CKPT = MODE == kFwdCkpt || MODE == kFwdOutCkpt || AGG;
+  constexpr bool USEC = OUT || AGG;   // C staged
   static_assert(MODE == kFwdOut || CKPT || CONV, "output, checkpoint and convolution modes");
+  static_assert(!AGG || NFIX == 16, "the reverse aggregates take N == 16");
   constexpr int T = kChunk;
   static_assert(T == 16, "one staged timestep per lane of a row");
   static_assert(!CKPT || 2 * kBwdBlock == T, "checkpoints are taken at half chunks");
@@ -138,7 +158,7 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
   constexpr int YP = kTile + 2;
   __shared__ float2 s_dx[2][T][DP];
   __shared__ __align__(16) float s_b[2][16][BR];
-  __shared__ __align__(16) float s_c[OUT ? 2 : 1][16][BR];
+  __shared__ __align__(16) float s_c[USEC ? 2 : 1][16][BR];
   // readout partials [k][j][i][column]: lane i of group k's partial for timestep 4k + j
   // of channel ch, at column ch + 2 (4k + i).  Rows of 96 words; the column shift puts
   // a half wave's stores (channels 4w, 4w + 1, all k and i) and the epilogue's reads
@@ -148,6 +168,11 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
   // checkpoint states of a chunk's two blocks, [half][state][channel], so that they
   // leave as whole rows of 64 channels (the layout the backward pass reads)
   __shared__ float s_ck[CKPT ? 2 : 1][2][16][YP];
+  // AGG: gy of [timestep][channel] (the recurrence reads timestep = state index: a row
+  // stride of 2 mod 32 words), and the per-wave sums of Delta*log2(e) over the second
+  // reverse segment
+  __shared__ float s_g[AGG ? 2 : 1][T][YP];
+  __shared__ float s_sum[AGG ? 16 : 1][kTile];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -182,13 +207,14 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
   const int64_t tok0 = (b * L + l_begin) * dim + dtile * kTile;
   const Tin* __restrict__ Xb = xg + tok0;
   const Tin* __restrict__ DTb = dtg + tok0;
-  const bool hasZ = OUT && zg != nullptr;
+  const bool hasZ = (OUT || AGG) && zg != nullptr;
   const Tin* __restrict__ Zb = hasZ ? zg + tok0 : xg + tok0;
   Tin* __restrict__ Yb = OUT ? yg + tok0 : nullptr;
-  // B/C staging loads: waves 0-7 load B, waves 8-15 load C (output modes), two rows
-  // each; lane j*N + n loads state n of row j
-  const Tin* __restrict__ BCs = ((w < 8 || !OUT) ? Bg : Cg) + (b * L + l_begin) * N;
-  const bool bcwave = w < 8 || OUT;
+  const Tin* __restrict__ DYb = AGG ? dyg + tok0 : xg + tok0;
+  // B/C staging loads: waves 0-7 load B, waves 8-15 load C (output and aggregate
+  // modes), two rows each; lane j*N + n loads state n of row j
+  const Tin* __restrict__ BCs = ((w < 8 || !USEC) ? Bg : Cg) + (b * L + l_begin) * N;
+  const bool bcwave = w < 8 || USEC;
   const int bcrow0 = 2 * (w & 7);
   const bool bclane = lane < 2 * N;
   const int bcj = bclane ? lane / N : 0;
@@ -243,9 +269,15 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
   }
   const Tin* __restrict__ Xrow = xg + b * L * dim + dtile * kTile;   // whole sequence of this row
 
+  // AGG: chunk c holds aggregate work when it lies in the second reverse segment
+  // (workgroup-uniform); the last chunk hands over the sums
+  auto agg_chunk = [&](int c) __attribute__((always_inline)) { return AGG && c * T >= sh.rseg_len; };
+  float qg = 0.f, pr = 1.f;          // G and the running product of Abar (lane = state)
+  float ssum = 0.f, scomp = 0.f;     // Kahan sum of the staged Delta*log2(e) (lane = channel)
+
   // Two register sets for the global loads, by chunk parity: chunk c's loads are
   // issued two iterations before its prologue consumes them.
-  Tin rx[2], rdt[2], rz[2], rbc[2];
+  Tin rx[2], rdt[2], rz[2], rbc[2], rdy[2];
   Tin rxc[2][KC];
   // Global loads of chunk c (parity S) for the prologue: x, dt, z of timestep w
   // (lane = channel) and this wave's B/C rows.  STEADY: chunk c is full.  Otherwise
@@ -271,7 +303,14 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
     }
     rdt[S] = ld_off(DTb + off, dlane);
     if constexpr (OUT) rz[S] = ld_off(Zb + off, dlane);
-    if (bcwave) {
+    const bool ag = agg_chunk(c);
+    if constexpr (AGG) {
+      if (ag) {
+        rdy[S] = ld_off(DYb + off, dlane);
+        rz[S] = ld_off(Zb + off, dlane);
+      }
+    }
+    if (bcwave && (!AGG || w < 8 || ag)) {
       const int r0 = c * T + bcrow0;
       if constexpr (STEADY) {
         rbc[S] = ld_off(BCs + static_cast<int64_t>(r0) * N, bcoff);
@@ -314,12 +353,27 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
       xv = lv ? xv : 0.f;
     }
     s_dx[P][w][lane] = make_float2(d2, EULER ? (d2 * kLn2) * xv : (STRUCT ? xv * rc : xv));
+    const bool ag = agg_chunk(c);
     if (bcwave && bclane) {
       const int t = bcrow0 + bcj;
       if (w < 8)
         s_b[P][bcn][t] = STRUCT ? to_f32(rbc[P]) * ra : to_f32(rbc[P]);
-      else if constexpr (OUT)
-        s_c[P][bcn][t] = to_f32(rbc[P]);
+      else if constexpr (USEC) {
+        if (!AGG || ag) s_c[P][bcn][t] = to_f32(rbc[P]);
+      }
+    }
+    if constexpr (AGG) {
+      if (ag) {
+        float gy = to_f32(rdy[P]);
+        if (hasZ) gy *= silu(to_f32(rz[P]));
+        if constexpr (!STEADY) gy = (c * T + w < seg_n) ? gy : 0.f;
+        s_g[P][w][lane] = gy;
+        const float yk = d2 - scomp;   // padded steps add 0
+        const float tk = ssum + yk;
+        scomp = (tk - ssum) - yk;
+        ssum = tk;
+        if (c == nchunks - 1) s_sum[w][lane] = ssum;
+      }
     }
     if constexpr (OUT) {
       if (hasZ)
@@ -374,11 +428,23 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
     // the chunk start, the LDS issue queue filled and the waves stalled behind it
     // (training shape 0.399 ms with all reads up front, 0.374 spread out).
     f32x4 bb[4], cb[4];
-    auto read_bc = [&](int m) __attribute__((always_inline)) {
+    // AGG: whether this chunk accumulates the reverse aggregate (C is read only then)
+    const bool aggc = agg_chunk(c);
+    auto read_bc = [&](int m, auto agc) __attribute__((always_inline)) {
       bb[m] = *reinterpret_cast<const f32x4*>(&s_b[P][ln][4 * m]);
-      if constexpr (OUT) cb[m] = *reinterpret_cast<const f32x4*>(&s_c[P][ln][4 * m]);
+      if constexpr (OUT || decltype(agc)::value) cb[m] = *reinterpret_cast<const f32x4*>(&s_c[P][ln][4 * m]);
     };
-    read_bc(0);
+    float sg = 0.f;   // AGG: gy of timestep ln for this lane's channel
+    if constexpr (AGG) {
+      if (aggc) {
+        read_bc(0, std::true_type{});
+        sg = s_g[P][ln][cr];
+      } else {
+        read_bc(0, std::false_type{});
+      }
+    } else {
+      read_bc(0, std::false_type{});
+    }
     float pg = 0.f, pd = 0.f;
     if constexpr (OUT) {
       pg = eg[Q];
@@ -393,15 +459,23 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
       ckpt_store(Par<Q>{}, c - 1);
     }
     float p[T];
+    // AGG: the reverse aggregate's share of step t (see the adjoint note)
+    auto agg_step = [&](auto tc, float e) __attribute__((always_inline)) {
+      constexpr int t = decltype(tc)::value;
+      pr = pr * e;
+      const float gc = row_bcast<t>(sg) * cb[t >> 2][t & 3];
+      qg = fmaf(pr, gc, qg);
+    };
     // the k-form steps; FAC: the staging holds x / c_d and B / a_n, so x_t B_t[n] as
-    // read is already k = x B / A
-    auto fast_steps = [&](auto facc) __attribute__((always_inline)) {
+    // read is already k = x B / A.  AGC: the chunk accumulates the reverse aggregate.
+    auto fast_steps = [&](auto facc, auto agc) __attribute__((always_inline)) {
       constexpr bool FAC = decltype(facc)::value;
+      constexpr bool AGC = decltype(agc)::value;
       static_for<0, T>([&](auto tc) {
         constexpr int t = decltype(tc)::value;
         if constexpr (t == 0 || t == 3 || t == 6) {
           __builtin_amdgcn_sched_barrier(0);
-          read_bc(t / 3 + 1);
+          read_bc(t / 3 + 1, agc);
           __builtin_amdgcn_sched_barrier(0);
         }
         if constexpr (t % kBwdBlock == 0) checkpoint(pc, t / kBwdBlock);
@@ -420,26 +494,19 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
           h = fmaf(e, h + k, -k);
         }
         if constexpr (OUT) p[t] = cb[t >> 2][t & 3] * h;
+        if constexpr (AGC) agg_step(tc, e);
       });
     };
-    if (EULER || !smallA) {
-      if constexpr (STRUCT) {
-        if (fac)   // workgroup-uniform
-          fast_steps(std::true_type{});
-        else
-          fast_steps(std::false_type{});
-      } else {
-        fast_steps(std::false_type{});
-      }
-    } else {
-      // some small |A| (A == 0 included) among the wave's channels: the explicit
-      // update h <- Abar h + phi B x with the accurate phi = (Abar - 1)/A of zoh_phi.
-      // The broadcast is taken once, by every lane, and zoh_phi forms both of its
-      // candidates before its select: a DPP read under a partial exec mask would see
-      // the inactive source lanes as zero.
-      read_bc(1);
-      read_bc(2);
-      read_bc(3);
+    // some small |A| (A == 0 included) among the wave's channels: the explicit
+    // update h <- Abar h + phi B x with the accurate phi = (Abar - 1)/A of zoh_phi.
+    // The broadcast is taken once, by every lane, and zoh_phi forms both of its
+    // candidates before its select: a DPP read under a partial exec mask would see
+    // the inactive source lanes as zero.
+    auto small_steps = [&](auto agc) __attribute__((always_inline)) {
+      constexpr bool AGC = decltype(agc)::value;
+      read_bc(1, agc);
+      read_bc(2, agc);
+      read_bc(3, agc);
       static_for<0, T>([&](auto tc) {
         constexpr int t = decltype(tc)::value;
         if constexpr (t % kBwdBlock == 0) checkpoint(pc, t / kBwdBlock);
@@ -452,7 +519,30 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
         const float xb = STRUCT ? xbs * am : xbs;
         h = fmaf(e, h, g * xb);
         if constexpr (OUT) p[t] = cb[t >> 2][t & 3] * h;
+        if constexpr (AGC) agg_step(tc, e);
       });
+    };
+    if (EULER || !smallA) {
+      if constexpr (STRUCT) {
+        if (fac)   // workgroup-uniform
+          fast_steps(std::true_type{}, std::false_type{});
+        else
+          fast_steps(std::false_type{}, std::false_type{});
+      } else if constexpr (AGG) {
+        if (aggc)
+          fast_steps(std::false_type{}, std::true_type{});
+        else
+          fast_steps(std::false_type{}, std::false_type{});
+      } else {
+        fast_steps(std::false_type{}, std::false_type{});
+      }
+    } else if constexpr (AGG) {
+      if (aggc)
+        small_steps(std::true_type{});
+      else
+        small_steps(std::false_type{});
+    } else {
+      small_steps(std::false_type{});
     }
     if constexpr (OUT) {
       float r[4];
@@ -462,13 +552,27 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) dst[j * 4 * YR] = r[j];
     }
+    if constexpr (AGG) {
+      // the last chunk: the second segment's G (lane = state), and its sum of
+      // Delta*log2(e) from the per-wave sums the chunk's prologue staged a barrier ago
+      if (aggc && c == nchunks - 1) {
+        const int64_t rowb = sh.batch + b;   // segment 1
+        if (drvalid) ragg_g[(rowb * dim + dr) * 16 + ln] = qg;
+        if (w == 0 && dvalid) {
+          float sum = 0.f;
+#pragma unroll
+          for (int q = 0; q < 16; ++q) sum += s_sum[q][lane];
+          ragg_s[rowb * dim + d] = sum;
+        }
+      }
+    }
     __syncthreads();
   };
 
   // zero once: the B/C rows of states past N (never written afterwards)
   for (int i = threadIdx.x; i < 2 * 16 * BR; i += 1024) {
     (&s_b[0][0][0])[i] = 0.f;
-    if constexpr (OUT) (&s_c[0][0][0])[i] = 0.f;
+    if constexpr (USEC) (&s_c[0][0][0])[i] = 0.f;
   }
   __syncthreads();
   if (nchunks > 0) {
@@ -504,11 +608,11 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
 
 template <typename Tin, int MODE, int NF, bool EU, bool ST = false>
 void launch_row_one(const FwdParams& p, dim3 grid, hipStream_t s) {
-  FwdShape sh{p.batch, p.L, p.dim, p.seg_len, p.ndtiles, p.nblk, p.N, p.nseg, p.dconv};
+  FwdShape sh{p.batch, p.L, p.dim, p.seg_len, p.ndtiles, p.nblk, p.rseg_len, p.N, p.nseg, p.dconv};
   hipLaunchKernelGGL((fwd_row_kernel<Tin, MODE, NF, EU, ST>), grid, dim3(1024), 0, s, static_cast<const Tin*>(p.x),
                      static_cast<const Tin*>(p.dt), static_cast<const Tin*>(p.z), static_cast<const Tin*>(p.B),
                      static_cast<const Tin*>(p.C), p.A, p.Dskip, p.bias, p.h_init, static_cast<Tin*>(p.y), p.h_last,
-                     p.ckpt, p.conv_w, p.conv_b, p.conv_s, sh);
+                     p.ckpt, p.conv_w, p.conv_b, p.conv_s, static_cast<const Tin*>(p.dy), p.ragg_g, p.ragg_s, sh);
 }
 
 // Launch of one (mode, discretization rule) variant of the row layout (N <= 16).
@@ -518,16 +622,26 @@ hipError_t launch_fwd_row(const FwdParams& p, bool bf16, hipStream_t s) {
   const int64_t nblocks = p.ndtiles * p.batch * p.nseg;
   if (nblocks <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(nblocks));
-  if (bf16) {
-    if (p.N == 16)
-      launch_row_one<bf16_t, MODE, 16, EU, ST>(p, grid, s);
+  if constexpr (MODE == kFwdCkptAgg) {
+    // N == 16, one forward segment, a second reverse segment starting at a chunk start
+    if (p.N != 16 || p.nseg != 1 || p.rseg_len <= 0 || p.rseg_len % kChunk != 0 || p.rseg_len >= p.L)
+      return hipErrorInvalidValue;
+    if (bf16)
+      launch_row_one<bf16_t, MODE, 16, EU>(p, grid, s);
     else
-      launch_row_one<bf16_t, MODE, 0, EU, ST>(p, grid, s);
+      launch_row_one<float, MODE, 16, EU>(p, grid, s);
   } else {
-    if (p.N == 16)
-      launch_row_one<float, MODE, 16, EU, ST>(p, grid, s);
-    else
-      launch_row_one<float, MODE, 0, EU, ST>(p, grid, s);
+    if (bf16) {
+      if (p.N == 16)
+        launch_row_one<bf16_t, MODE, 16, EU, ST>(p, grid, s);
+      else
+        launch_row_one<bf16_t, MODE, 0, EU, ST>(p, grid, s);
+    } else {
+      if (p.N == 16)
+        launch_row_one<float, MODE, 16, EU, ST>(p, grid, s);
+      else
+        launch_row_one<float, MODE, 0, EU, ST>(p, grid, s);
+    }
   }
   return hipGetLastError();
 }

@@ -17,6 +17,8 @@ constexpr int kFwdAgg = 1;    // per-segment aggregates for the two-level scan
 constexpr int kFwdCkpt = 2;   // states entering every kBwdBlock steps, for the backward pass
 constexpr int kFwdOutCkpt = 3;  // y and the final state, and the kFwdCkpt states as well
 constexpr int kFwdOutConv = 4;  // kFwdOut with the convolution prologue (row layout only)
+constexpr int kFwdCkptAgg = 5;  // kFwdCkpt, and the backward pass's aggregates of its second
+                                // reverse segment (row layout, N == 16, one forward segment)
 
 struct FwdParams {
   const void* x;
@@ -38,6 +40,13 @@ struct FwdParams {
   const float* conv_b;    // nullable: [dim]
   const float* conv_s;    // nullable: raw inputs before the sequence [batch][dim][dconv-1]
   int dconv;
+  // kFwdCkptAgg: the output gradient, and the reverse aggregates (as the backward
+  // pass's ragg_g / ragg_s, segment 1) of the second of two reverse segments, which
+  // starts at rseg_len (a multiple of kChunk below L)
+  const void* dy;
+  float* ragg_g;
+  float* ragg_s;
+  int64_t rseg_len;
   int64_t batch, L, dim;
   int64_t seg_len;        // timesteps per segment (multiple of kChunk unless nseg == 1)
   int64_t ndtiles;        // ceil(dim / kTile)
@@ -52,7 +61,7 @@ struct FwdParams {
 // Sizes passed by value to the forward kernels (pointers go as separate
 // restrict-qualified arguments so the compiler can keep B/C loads scalar).
 struct FwdShape {
-  int64_t batch, L, dim, seg_len, ndtiles, nblk;
+  int64_t batch, L, dim, seg_len, ndtiles, nblk, rseg_len;
   int N, nseg, dconv;
 };
 
@@ -112,6 +121,7 @@ struct BwdParams {
   int N;
   int nseg;
   bool euler;
+  bool agg_done;          // ragg_g / ragg_s already written (by the kFwdCkptAgg checkpoint pass)
 };
 
 struct BwdShape {
@@ -130,6 +140,8 @@ bool fwd_row_layout(const FwdParams& p);
 hipError_t launch_fwd_main(const FwdParams& p, bool bf16, hipStream_t s);
 hipError_t launch_fwd_aggregate(const FwdParams& p, bool bf16, hipStream_t s);
 hipError_t launch_fwd_checkpoints(const FwdParams& p, bool bf16, hipStream_t s);
+// kFwdCkptAgg: N == 16, nseg == 1, rseg_len a positive multiple of kChunk below L
+hipError_t launch_fwd_checkpoints_agg(const FwdParams& p, bool bf16, hipStream_t s);
 hipError_t launch_fwd_carry(const float* agg_h, const float* agg_s, const float* A, const float* h_init,
                             float* carry, int64_t batch, int64_t dim, int N, int nseg, hipStream_t s);
 hipError_t launch_fill_state(float* dst, const float* src, int64_t n, hipStream_t s);

@@ -82,6 +82,30 @@ def test_bwd_segmented_checkpoints(ss, orc, euler):
     check_bwd(ss, orc, w, h0=h0, euler=euler)
 
 
+# The checkpoint pass that also forms the reverse segment aggregates runs where the
+# checkpoint sweep is one segment (at least one workgroup per CU: batch x 64-channel
+# tiles in [256, 512) on 256 CUs) and the reverse pass has two segments of whole
+# chunks.  (4, 90, 4096): 256 workgroups, reverse segments of 48 and 42 steps (the
+# second ends in a ragged chunk).
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("euler", [False, True])
+def test_bwd_aggregates_in_checkpoint_pass(ss, orc, dtype, euler):
+    w = W.make_scan_inputs(4, 90, 4096, 16, dtype, seed=510, name="bwd checkpoint pass with aggregates")
+    h0 = np.random.default_rng(10).standard_normal((4, 4096, 16)).astype(np.float32)
+    check_bwd(ss, orc, w, h0=h0, euler=euler)
+
+
+def test_bwd_aggregates_in_checkpoint_pass_small_A_no_gate(ss, orc):
+    # the same path with no z (gy = dy) and no final-state gradient, and channels whose
+    # waves take the small-|A| form of the step (A = 0 included)
+    w = W.make_scan_inputs(4, 96, 4096, 16, "f32", seed=511, with_z=False, name="bwd checkpoint pass, small A")
+    w.A = w.A.copy()
+    w.A[8:12, :] = -1e-3
+    w.A[300, 4] = 0.0
+    w.A[2049, :] = -1e-5
+    check_bwd(ss, orc, w, with_dlast=False)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_bwd_optional_inputs_absent(ss, orc, dtype):
     w = W.make_scan_inputs(1, 70, 64, 16, dtype, seed=502, with_z=False, with_D=False, with_bias=False,
