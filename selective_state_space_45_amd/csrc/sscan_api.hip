@@ -531,11 +531,11 @@ int bwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dty
   const int64_t nblk = (seqlen + sscan::kBwdBlock - 1) / sscan::kBwdBlock;
   const int64_t ndt = (dim + sscan::kTile - 1) / sscan::kTile;
   const float* ckpt = saved ? ckpt_in : reinterpret_cast<const float*>(ws + lo.ckpt);
-  // The checkpoint pass also forms the reverse aggregates when it runs as one sweep
-  // over the sequence and the reverse pass has two segments (the count bwd_segments
-  // gives for one to two workgroups per CU), N == 16, the second starting at a chunk
-  // start: the sweep already forms every Abar, and the separate aggregate sweep is
-  // skipped.
+  // The checkpoint pass also forms the reverse pass's segment carries when it runs as
+  // one sweep over the sequence and the reverse pass has two segments (the count
+  // bwd_segments gives for one to two workgroups per CU), N == 16, the second starting
+  // at a chunk start: the sweep already forms every Abar, and the separate aggregate
+  // sweep and carry kernel are skipped.
   const int64_t rseg_len = lo.seg_blocks * sscan::kBwdBlock;
   const bool agg_in_ckpt = !saved && lo.nseg == 1 && N == 16 && lo.bseg == 2 && rseg_len % sscan::kChunk == 0;
   hipError_t e;
@@ -573,8 +573,8 @@ int bwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dty
   if (agg_in_ckpt) {
     p.z = z;
     p.dy = dy;
-    p.ragg_g = reinterpret_cast<float*>(ws + lo.rg);
-    p.ragg_s = reinterpret_cast<float*>(ws + lo.rs);
+    p.dlast = dlast_state;
+    p.gin = reinterpret_cast<float*>(ws + lo.gin);
     p.rseg_len = rseg_len;
     e = sscan::launch_fwd_checkpoints_agg(p, bf16, s);
   } else {
@@ -603,7 +603,7 @@ int bwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dty
   q.ragg_g = reinterpret_cast<float*>(ws + lo.rg);
   q.ragg_s = reinterpret_cast<float*>(ws + lo.rs);
   q.gin = reinterpret_cast<float*>(ws + lo.gin);
-  q.agg_done = agg_in_ckpt;
+  q.carry_done = agg_in_ckpt;
   e = sscan::launch_bwd(q, bf16, s);
   if (e != hipSuccess) return hip_fail(e, "backward launch");
   return ok();

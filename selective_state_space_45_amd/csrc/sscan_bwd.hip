@@ -885,69 +885,89 @@ __global__ __launch_bounds__(256) void bwd_carry_kernel(const float* __restrict_
   }
 }
 
-// dB[b][l][n] = sum over channel tiles of the partials (fixed order), in the token
-// dtype; one thread per (b, n, l), l fastest, so the partial reads coalesce.
-template <typename Tin>
-__global__ __launch_bounds__(256) void bwd_reduce_bc(const float* __restrict__ gBp, const float* __restrict__ gCp,
-                                                     Tin* __restrict__ dB, Tin* __restrict__ dC, int64_t batch,
-                                                     int64_t L, int N, int64_t ndtiles) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;   // (b * N + n) * L + l
+// The reductions after the reverse pass, in one launch.
+//  * dB[b][l][n], dC[b][l][n] = sums over channel tiles of the partials (fixed order),
+//    in the token dtype.  One thread per (b, n) and V consecutive l (V = 4 when L is a
+//    multiple of 4: 16-byte partial loads), l fastest, so the partial reads coalesce;
+//    the tiles are read in groups of G, whose loads are issued together and then added
+//    in tile order (the same order as one at a time, so the sums are unchanged).
+//  * dA[d][n], dD[d], dbias[d] = sums over (segment, batch row) partials (fixed order),
+//    by the grid's last workgroups (from bc_blocks on): one thread per (n, d), d
+//    fastest, so the partial reads ([row][n][dim]) coalesce.
+template <typename Tin, int V>
+__global__ __launch_bounds__(256) void bwd_reduce(const float* __restrict__ gBp, const float* __restrict__ gCp,
+                                                  Tin* __restrict__ dB, Tin* __restrict__ dC, int64_t batch,
+                                                  int64_t L, int N, int64_t ndtiles, unsigned bc_blocks,
+                                                  const float* __restrict__ gAp, const float* __restrict__ gDp,
+                                                  const float* __restrict__ gbp, float* __restrict__ dA,
+                                                  float* __restrict__ dD, float* __restrict__ dbias, int64_t rows,
+                                                  int64_t dim) {
+  constexpr int G = 8;
+  if (blockIdx.x >= bc_blocks) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x - bc_blocks) * blockDim.x + threadIdx.x;   // n * dim + d
+    if (i >= dim * N) return;
+    const int n = static_cast<int>(i / dim);
+    const int64_t d = i - static_cast<int64_t>(n) * dim;
+    float s = 0.f;
+    for (int64_t r0 = 0; r0 < rows; r0 += G) {
+      float v[G];
+#pragma unroll
+      for (int k = 0; k < G; ++k) v[k] = (r0 + k < rows) ? gAp[(r0 + k) * N * dim + i] : 0.f;
+#pragma unroll
+      for (int k = 0; k < G; ++k)
+        if (r0 + k < rows) s += v[k];
+    }
+    dA[d * N + n] = s;
+    if (n == 0) {
+      float sD = 0.f, sb = 0.f;
+      for (int64_t r0 = 0; r0 < rows; r0 += G) {
+        float vD[G], vb[G];
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+          vD[k] = (r0 + k < rows) ? gDp[(r0 + k) * dim + d] : 0.f;
+          vb[k] = (r0 + k < rows) ? gbp[(r0 + k) * dim + d] : 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < G; ++k)
+          if (r0 + k < rows) {
+            sD += vD[k];
+            sb += vb[k];
+          }
+      }
+      if (dD) dD[d] = sD;
+      if (dbias) dbias[d] = sb;
+    }
+    return;
+  }
   const int64_t per_tile = batch * N * L;
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * V;   // (b * N + n) * L + l
   if (i >= per_tile) return;
+  typedef float vec __attribute__((ext_vector_type(V)));
+  vec sB = {}, sC = {};
+  for (int64_t k0 = 0; k0 < ndtiles; k0 += G) {
+    vec vb[G], vc[G];
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      if (k0 + k < ndtiles) {
+        vb[k] = *reinterpret_cast<const vec*>(gBp + (k0 + k) * per_tile + i);
+        vc[k] = *reinterpret_cast<const vec*>(gCp + (k0 + k) * per_tile + i);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < G; ++k)
+      if (k0 + k < ndtiles) {
+        sB += vb[k];
+        sC += vc[k];
+      }
+  }
   const int64_t l = i % L;
   const int64_t bn = i / L;
   const int64_t n = bn % N, b = bn / N;
-  float sB = 0.f, sC = 0.f;
-  for (int64_t k = 0; k < ndtiles; ++k) {
-    sB += gBp[k * per_tile + i];
-    sC += gCp[k * per_tile + i];
-  }
-  const int64_t o = (b * L + l) * N + n;
-  store_val(&dB[o], sB);
-  store_val(&dC[o], sC);
-}
-
-// dA[d][n], dD[d], dbias[d] = sums over (segment, batch row) partials (fixed order).
-// One thread per (n, d), d fastest, so that the partial reads ([row][n][dim]) coalesce.
-__global__ __launch_bounds__(256) void bwd_reduce_params(const float* __restrict__ gAp, const float* __restrict__ gDp,
-                                                         const float* __restrict__ gbp, float* __restrict__ dA,
-                                                         float* __restrict__ dD, float* __restrict__ dbias,
-                                                         int64_t rows, int64_t dim, int N) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;   // n * dim + d
-  if (i >= dim * N) return;
-  const int n = static_cast<int>(i / dim);
-  const int64_t d = i - static_cast<int64_t>(n) * dim;
-  // rows in groups of G, loaded together and then added in row order (the same
-  // order as one at a time, so the sums are unchanged)
-  constexpr int G = 8;
-  float s = 0.f;
-  for (int64_t r0 = 0; r0 < rows; r0 += G) {
-    float v[G];
 #pragma unroll
-    for (int k = 0; k < G; ++k) v[k] = (r0 + k < rows) ? gAp[(r0 + k) * N * dim + i] : 0.f;
-#pragma unroll
-    for (int k = 0; k < G; ++k)
-      if (r0 + k < rows) s += v[k];
-  }
-  dA[d * N + n] = s;
-  if (n == 0) {
-    float sD = 0.f, sb = 0.f;
-    for (int64_t r0 = 0; r0 < rows; r0 += G) {
-      float vD[G], vb[G];
-#pragma unroll
-      for (int k = 0; k < G; ++k) {
-        vD[k] = (r0 + k < rows) ? gDp[(r0 + k) * dim + d] : 0.f;
-        vb[k] = (r0 + k < rows) ? gbp[(r0 + k) * dim + d] : 0.f;
-      }
-#pragma unroll
-      for (int k = 0; k < G; ++k)
-        if (r0 + k < rows) {
-          sD += vD[k];
-          sb += vb[k];
-        }
-    }
-    if (dD) dD[d] = sD;
-    if (dbias) dbias[d] = sb;
+  for (int v = 0; v < V; ++v) {
+    const int64_t o = (b * L + l + v) * N + n;
+    store_val(&dB[o], sB[v]);
+    store_val(&dC[o], sC[v]);
   }
 }
 
@@ -956,22 +976,20 @@ namespace {
 template <typename Tin, int NW, int NF, bool EU>
 void launch_bwd_one(const BwdParams& p, hipStream_t s) {
   BwdShape sh{p.batch, p.L, p.dim, p.ndtiles, p.nblk, p.seg_blocks, p.N, p.nseg};
-  if (p.nseg > 1) {
+  if (p.nseg > 1 && !p.carry_done) {   // else gin was formed by the checkpoint pass
     const dim3 agrid(static_cast<unsigned>(p.ndtiles * p.batch * (p.nseg - 1)));
-    if (!p.agg_done) {   // else formed by the checkpoint pass
-      if constexpr (NF == 16) {
-        hipLaunchKernelGGL((bwd_agg_row_kernel<Tin>), agrid, dim3(1024), 0, s, static_cast<const Tin*>(p.dt),
-                           static_cast<const Tin*>(p.z), static_cast<const Tin*>(p.C), static_cast<const Tin*>(p.dy),
-                           p.A, p.bias, p.ragg_g, p.ragg_s, sh);
-      } else {
-        // one state per wave in the aggregate pass: twice the reverse pass's waves, for
-        // occupancy (measured: two states per wave was no faster on the training shape)
-        constexpr int AS = 1;
-        constexpr int AW = NW * kBwdSpw / AS;
-        hipLaunchKernelGGL((bwd_agg_kernel<Tin, AW, AS, NF>), agrid, dim3(AW * 64), 0, s,
-                           static_cast<const Tin*>(p.dt), static_cast<const Tin*>(p.z), static_cast<const Tin*>(p.C),
-                           static_cast<const Tin*>(p.dy), p.A, p.bias, p.ragg_g, p.ragg_s, sh);
-      }
+    if constexpr (NF == 16) {
+      hipLaunchKernelGGL((bwd_agg_row_kernel<Tin>), agrid, dim3(1024), 0, s, static_cast<const Tin*>(p.dt),
+                         static_cast<const Tin*>(p.z), static_cast<const Tin*>(p.C), static_cast<const Tin*>(p.dy),
+                         p.A, p.bias, p.ragg_g, p.ragg_s, sh);
+    } else {
+      // one state per wave in the aggregate pass: twice the reverse pass's waves, for
+      // occupancy (measured: two states per wave was no faster on the training shape)
+      constexpr int AS = 1;
+      constexpr int AW = NW * kBwdSpw / AS;
+      hipLaunchKernelGGL((bwd_agg_kernel<Tin, AW, AS, NF>), agrid, dim3(AW * 64), 0, s, static_cast<const Tin*>(p.dt),
+                         static_cast<const Tin*>(p.z), static_cast<const Tin*>(p.C), static_cast<const Tin*>(p.dy),
+                         p.A, p.bias, p.ragg_g, p.ragg_s, sh);
     }
     const int64_t total = p.batch * p.dim * p.N;
     hipLaunchKernelGGL(bwd_carry_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s,
@@ -1010,14 +1028,19 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t nbl = p.batch * p.N * p.L;
-  hipLaunchKernelGGL((bwd_reduce_bc<Tin>), dim3(static_cast<unsigned>((nbl + 255) / 256)), dim3(256), 0, s,
-                     p.gB_part, p.gC_part, static_cast<Tin*>(p.dB), static_cast<Tin*>(p.dC), p.batch, p.L, p.N,
-                     p.ndtiles);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const int64_t ndn = p.dim * p.N;
-  hipLaunchKernelGGL(bwd_reduce_params, dim3(static_cast<unsigned>((ndn + 255) / 256)), dim3(256), 0, s, p.gA_part,
-                     p.gD_part, p.gbias_part, p.dA, p.dD, p.dbias, p.batch * p.nseg, p.dim, p.N);
+  const unsigned params_blocks = static_cast<unsigned>((ndn + 255) / 256);
+  if (p.L % 4 == 0) {
+    const unsigned bc_blocks = static_cast<unsigned>((nbl / 4 + 255) / 256);
+    hipLaunchKernelGGL((bwd_reduce<Tin, 4>), dim3(bc_blocks + params_blocks), dim3(256), 0, s, p.gB_part, p.gC_part,
+                       static_cast<Tin*>(p.dB), static_cast<Tin*>(p.dC), p.batch, p.L, p.N, p.ndtiles, bc_blocks,
+                       p.gA_part, p.gD_part, p.gbias_part, p.dA, p.dD, p.dbias, p.batch * p.nseg, p.dim);
+  } else {
+    const unsigned bc_blocks = static_cast<unsigned>((nbl + 255) / 256);
+    hipLaunchKernelGGL((bwd_reduce<Tin, 1>), dim3(bc_blocks + params_blocks), dim3(256), 0, s, p.gB_part, p.gC_part,
+                       static_cast<Tin*>(p.dB), static_cast<Tin*>(p.dC), p.batch, p.L, p.N, p.ndtiles, bc_blocks,
+                       p.gA_part, p.gD_part, p.gbias_part, p.dA, p.dD, p.dbias, p.batch * p.nseg, p.dim);
+  }
   return hipGetLastError();
 }
 

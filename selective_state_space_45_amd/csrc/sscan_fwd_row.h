@@ -124,9 +124,10 @@ __device__ __forceinline__ void row_reduce_partial16(const float (&p)[16], float
 // segment's first step.  G is a sum over the segment in any order; here it is
 // accumulated forward, during the checkpoint sweep that already forms every Abar_t: a
 // running product pr <- pr Abar_t and G <- G + pr C_t gy_t, three VALU per state and
-// step, instead of a separate reverse sweep that recomputes Delta and Abar.  One
-// forward segment (the sweep starts at position 0); rseg_len is a multiple of kChunk,
-// so the second segment starts at a chunk start and ends with the last chunk.
+// step, instead of a separate reverse sweep that recomputes Delta and Abar.  The
+// kernel then writes the reverse pass's two segment carries itself.  One forward
+// segment (the sweep starts at position 0); rseg_len is a multiple of kChunk, so the
+// second segment starts at a chunk start and ends with the last chunk.
 template <typename Tin, int MODE, int NFIX, bool EULER, bool STRUCT = false>
 __global__ __launch_bounds__(1024) void fwd_row_kernel(
     const Tin* __restrict__ xg, const Tin* __restrict__ dtg, const Tin* __restrict__ zg,
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
     const float* __restrict__ Dg, const float* __restrict__ biasg, const float* __restrict__ h_init,
     Tin* __restrict__ yg, float* __restrict__ h_last, float* __restrict__ ckpt, const float* __restrict__ conv_w,
     const float* __restrict__ conv_b, const float* __restrict__ conv_s, const Tin* __restrict__ dyg,
-    float* __restrict__ ragg_g, float* __restrict__ ragg_s, FwdShape sh) {
+    const float* __restrict__ dlast, float* __restrict__ gin, FwdShape sh) {
   constexpr bool CONV = MODE == kFwdOutConv;
   constexpr bool OUT = MODE == kFwdOut || MODE == kFwdOutCkpt || CONV;
   constexpr bool AGG = MODE == kFwdCkptAgg;
@@ -552,20 +553,6 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) dst[j * 4 * YR] = r[j];
     }
-    if constexpr (AGG) {
-      // the last chunk: the second segment's G (lane = state), and its sum of
-      // Delta*log2(e) from the per-wave sums the chunk's prologue staged a barrier ago
-      if (aggc && c == nchunks - 1) {
-        const int64_t rowb = sh.batch + b;   // segment 1
-        if (drvalid) ragg_g[(rowb * dim + dr) * 16 + ln] = qg;
-        if (w == 0 && dvalid) {
-          float sum = 0.f;
-#pragma unroll
-          for (int q = 0; q < 16; ++q) sum += s_sum[q][lane];
-          ragg_s[rowb * dim + d] = sum;
-        }
-      }
-    }
     __syncthreads();
   };
 
@@ -604,6 +591,22 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
   if constexpr (OUT) {
     if (h_last && seg == sh.nseg - 1 && drvalid && nlive) h_last[(b * dim + dr) * N + ln] = h;
   }
+  if constexpr (AGG) {
+    // The reverse pass's segment carries, formed as its carry kernel forms them: the
+    // gradient entering the end of segment 1 is dLoss/d(last state) (or 0), the one
+    // entering the end of segment 0 is exp2(A S) gl + G, with S the second segment's sum
+    // of Delta*log2(e): the per-wave sums its last prologue staged (the last chunk's
+    // barrier has passed), added in wave order.
+    if (nchunks > 0 && agg_chunk(nchunks - 1) && drvalid) {
+      float S = 0.f;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) S += s_sum[q][cr];
+      const int64_t i = (b * dim + dr) * 16 + ln;
+      const float gl = dlast ? dlast[i] : 0.f;
+      gin[sh.batch * dim * 16 + i] = gl;
+      gin[i] = fmaf(hw_exp2(Av * S), gl, qg);
+    }
+  }
 }
 
 template <typename Tin, int MODE, int NF, bool EU, bool ST = false>
@@ -612,7 +615,7 @@ void launch_row_one(const FwdParams& p, dim3 grid, hipStream_t s) {
   hipLaunchKernelGGL((fwd_row_kernel<Tin, MODE, NF, EU, ST>), grid, dim3(1024), 0, s, static_cast<const Tin*>(p.x),
                      static_cast<const Tin*>(p.dt), static_cast<const Tin*>(p.z), static_cast<const Tin*>(p.B),
                      static_cast<const Tin*>(p.C), p.A, p.Dskip, p.bias, p.h_init, static_cast<Tin*>(p.y), p.h_last,
-                     p.ckpt, p.conv_w, p.conv_b, p.conv_s, static_cast<const Tin*>(p.dy), p.ragg_g, p.ragg_s, sh);
+                     p.ckpt, p.conv_w, p.conv_b, p.conv_s, static_cast<const Tin*>(p.dy), p.dlast, p.gin, sh);
 }
 
 // Launch of one (mode, discretization rule) variant of the row layout (N <= 16).

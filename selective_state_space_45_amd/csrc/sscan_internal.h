@@ -17,8 +17,8 @@ constexpr int kFwdAgg = 1;    // per-segment aggregates for the two-level scan
 constexpr int kFwdCkpt = 2;   // states entering every kBwdBlock steps, for the backward pass
 constexpr int kFwdOutCkpt = 3;  // y and the final state, and the kFwdCkpt states as well
 constexpr int kFwdOutConv = 4;  // kFwdOut with the convolution prologue (row layout only)
-constexpr int kFwdCkptAgg = 5;  // kFwdCkpt, and the backward pass's aggregates of its second
-                                // reverse segment (row layout, N == 16, one forward segment)
+constexpr int kFwdCkptAgg = 5;  // kFwdCkpt, and the backward pass's segment carries for two
+                                // reverse segments (row layout, N == 16, one forward segment)
 
 struct FwdParams {
   const void* x;
@@ -40,12 +40,12 @@ struct FwdParams {
   const float* conv_b;    // nullable: [dim]
   const float* conv_s;    // nullable: raw inputs before the sequence [batch][dim][dconv-1]
   int dconv;
-  // kFwdCkptAgg: the output gradient, and the reverse aggregates (as the backward
-  // pass's ragg_g / ragg_s, segment 1) of the second of two reverse segments, which
-  // starts at rseg_len (a multiple of kChunk below L)
+  // kFwdCkptAgg: the output gradient and dLoss/d(last state) (nullable), and the
+  // backward pass's gin [2][batch][dim][N] (as its carry kernel forms it) for two
+  // reverse segments, the second starting at rseg_len (a multiple of kChunk below L)
   const void* dy;
-  float* ragg_g;
-  float* ragg_s;
+  const float* dlast;
+  float* gin;
   int64_t rseg_len;
   int64_t batch, L, dim;
   int64_t seg_len;        // timesteps per segment (multiple of kChunk unless nseg == 1)
@@ -121,7 +121,7 @@ struct BwdParams {
   int N;
   int nseg;
   bool euler;
-  bool agg_done;          // ragg_g / ragg_s already written (by the kFwdCkptAgg checkpoint pass)
+  bool carry_done;        // gin already written (by the kFwdCkptAgg checkpoint pass)
 };
 
 struct BwdShape {
