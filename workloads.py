@@ -174,6 +174,64 @@ def make_scan_inputs(batch: int, seqlen: int, dim: int, dstate: int, dtype: str 
                       dt_bias=bias, meta=dict(seed=seed, step=step, delta_range=delta_range))
 
 
+def device_scan_inputs(batch: int, seqlen: int, dim: int, dstate: int, seed: int,
+                       delta_range: Tuple[float, float] = (1e-3, 1e-1), device: str = "cuda") -> Dict:
+    """Seeded bf16 inputs drawn on the device, for shapes whose tensors are too large
+    to sample on the host (several GB each).  The recipe of make_scan_inputs with
+    step == "logu" (x, z, B, C ~ N(0, 1); per-channel bias = softplus^-1(Delta0),
+    dt = softplus^-1(Delta*) - bias with Delta0, Delta* ~ logU[delta_range];
+    A = -(n + 1); D ~ N(0, 1)), drawn with torch's device generator seeded by `seed`,
+    one batch row at a time, in float32 and rounded once to bf16.  Also an upstream
+    gradient dy ~ N(0, 1) (bf16) and dlast ~ N(0, 1) (float32) for the backward pass.
+    Returns a dict of device tensors: x, dt, z, dy, B, C (bf16); A, D, dt_bias, dlast
+    (float32)."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    f32, bf = torch.float32, torch.bfloat16
+    llo, lhi = float(np.log(delta_range[0])), float(np.log(delta_range[1]))
+
+    def logu(shape):
+        return torch.exp(llo + (lhi - llo) * torch.rand(shape, generator=gen, device=device, dtype=f32))
+
+    d0 = logu((dim,))
+    bias = torch.log(torch.expm1(d0))
+    out = {name: torch.empty((batch, seqlen, dim), dtype=bf, device=device) for name in ("x", "dt", "z", "dy")}
+    for b in range(batch):
+        out["x"][b] = torch.randn((seqlen, dim), generator=gen, device=device, dtype=f32).to(bf)
+        out["z"][b] = torch.randn((seqlen, dim), generator=gen, device=device, dtype=f32).to(bf)
+        out["dt"][b] = (torch.log(torch.expm1(logu((seqlen, dim)))) - bias[None, :]).to(bf)
+        out["dy"][b] = torch.randn((seqlen, dim), generator=gen, device=device, dtype=f32).to(bf)
+    out["B"] = torch.randn((batch, seqlen, dstate), generator=gen, device=device, dtype=f32).to(bf)
+    out["C"] = torch.randn((batch, seqlen, dstate), generator=gen, device=device, dtype=f32).to(bf)
+    out["A"] = torch.from_numpy(s4d_real_A(dim, dstate)).to(device)
+    out["D"] = torch.randn((dim,), generator=gen, device=device, dtype=f32)
+    out["dt_bias"] = bias
+    out["dlast"] = torch.randn((batch, dim, dstate), generator=gen, device=device, dtype=f32)
+    return out
+
+
+def device_step_inputs(batch: int, dim: int, dstate: int, seed: int, device: str = "cuda") -> Dict:
+    """Seeded inputs of one decode step drawn on the device, for states too large to
+    sample on the host: the recipe of DecodeWorkload (state ~ 0.1 N(0, 1) float32;
+    x, dt, z [batch, dim] and B, C [batch, dstate] ~ N(0, 1) in bf16; A = -(n + 1);
+    D ~ N(0, 1); no bias), drawn with torch's device generator seeded by `seed`."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    f32, bf = torch.float32, torch.bfloat16
+    state = torch.empty((batch, dim, dstate), dtype=f32, device=device)
+    for b in range(batch):
+        state[b] = 0.1 * torch.randn((dim, dstate), generator=gen, device=device, dtype=f32)
+    out = {"state": state}
+    for name, shape in (("x", (batch, dim)), ("dt", (batch, dim)), ("z", (batch, dim)), ("B", (batch, dstate)),
+                        ("C", (batch, dstate))):
+        out[name] = torch.randn(shape, generator=gen, device=device, dtype=f32).to(bf)
+    out["A"] = torch.from_numpy(s4d_real_A(dim, dstate)).to(device)
+    out["D"] = torch.randn((dim,), generator=gen, device=device, dtype=f32)
+    return out
+
+
 # ----------------------------------------------------------------------------
 # The five named workloads.
 # ----------------------------------------------------------------------------
