@@ -269,6 +269,10 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
     cbias = conv_b ? conv_b[dd] : 0.f;
   }
   const Tin* __restrict__ Xrow = xg + b * L * dim + dtile * kTile;   // whole sequence of this row
+  // CONV: element offset back from position l to tap k's input (taps past K: none)
+  int64_t tapoff[KC];
+#pragma unroll
+  for (int k = 0; k < KC; ++k) tapoff[k] = ((K - 1 - k) < 0 ? 0 : (K - 1 - k)) * dim;
 
   // AGG: chunk c holds aggregate work when it lies in the second reverse segment
   // (workgroup-uniform); the last chunk hands over the sums
@@ -276,28 +280,51 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
   float qg = 0.f, pr = 1.f;          // G and the running product of Abar (lane = state)
   float ssum = 0.f, scomp = 0.f;     // Kahan sum of the staged Delta*log2(e) (lane = channel)
 
+  // RUN: steady iterations address their chunks through running element offsets,
+  // advanced by adds in the steady loop, instead of 64-bit products per chunk:
+  // run_dim = c T dim and run_bc = c T N for the iteration of chunk c, which loads
+  // chunk c + 3 (timestep w: off_g; B/C rows: off_bc) and stores y of chunk c - 1
+  // (off_e).  Not in the convolution and aggregate modes, whose registers are
+  // already full (there the offsets took the conv variant to 128 VGPRs and a spill).
+  constexpr bool RUN = !CONV && !AGG;
+  const int64_t Tdim = static_cast<int64_t>(T) * dim;
+  const int64_t TN = static_cast<int64_t>(T) * N;
+  const int64_t off_g = 3 * Tdim + static_cast<int64_t>(w) * dim;
+  const int64_t off_e = static_cast<int64_t>(w) * dim - Tdim;
+  const int64_t off_bc = 3 * TN + static_cast<int64_t>(bcrow0) * N;
+  int64_t run_dim = 0, run_bc = 0;
   // Two register sets for the global loads, by chunk parity: chunk c's loads are
   // issued two iterations before its prologue consumes them.
   Tin rx[2], rdt[2], rz[2], rbc[2], rdy[2];
   Tin rxc[2][KC];
   // Global loads of chunk c (parity S) for the prologue: x, dt, z of timestep w
-  // (lane = channel) and this wave's B/C rows.  STEADY: chunk c is full.  Otherwise
+  // (lane = channel) and this wave's B/C rows.  STEADY: chunk c is full, and is the
+  // chunk three past the steady iteration's own (the running offsets under RUN).  Otherwise
   // positions past the segment end read its last row (those steps become identities
   // in the prologue).
   auto gload = [&](auto sc, auto steadyc, int c) __attribute__((always_inline)) {
     constexpr int S = decltype(sc)::value;
     constexpr bool STEADY = decltype(steadyc)::value;
     const int l = c * T + w;
-    const int64_t off = static_cast<int64_t>(STEADY ? l : (l < seg_n ? l : seg_n - 1)) * dim;
+    const int64_t off = (STEADY && RUN) ? run_dim + off_g
+                                        : static_cast<int64_t>(STEADY ? l : (l < seg_n ? l : seg_n - 1)) * dim;
     if constexpr (CONV) {
       // raw inputs of the window l - (K-1) .. l, from positions clamped at the sequence
-      // start (replaced from conv_s in the prologue); taps past K load position l
+      // start (replaced from conv_s in the prologue); taps past K load position l.  A
+      // steady chunk is the fourth or later of its segment, so its window never reaches
+      // before the sequence start: one base and the hoisted tap offsets.
       const int64_t lg = l_begin + (STEADY ? l : (l < seg_n ? l : seg_n - 1));
+      if constexpr (STEADY) {
+        const Tin* __restrict__ xl = Xrow + lg * dim;
 #pragma unroll
-      for (int k = 0; k < KC; ++k) {
-        const int back = (K - 1 - k) < 0 ? 0 : (K - 1 - k);
-        const int64_t pos = lg - (back <= lg ? back : lg);
-        rxc[S][k] = ld_off(Xrow + pos * dim, dlane);
+        for (int k = 0; k < KC; ++k) rxc[S][k] = ld_off(xl - tapoff[k], dlane);
+      } else {
+#pragma unroll
+        for (int k = 0; k < KC; ++k) {
+          const int back = (K - 1 - k) < 0 ? 0 : (K - 1 - k);
+          const int64_t pos = lg - (back <= lg ? back : lg);
+          rxc[S][k] = ld_off(Xrow + pos * dim, dlane);
+        }
       }
     } else {
       rx[S] = ld_off(Xb + off, dlane);
@@ -314,7 +341,7 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
     if (bcwave && (!AGG || w < 8 || ag)) {
       const int r0 = c * T + bcrow0;
       if constexpr (STEADY) {
-        rbc[S] = ld_off(BCs + static_cast<int64_t>(r0) * N, bcoff);
+        rbc[S] = ld_off(BCs + (RUN ? run_bc + off_bc : static_cast<int64_t>(r0) * N), bcoff);
       } else {
         const int rr = r0 + bcj < seg_n ? r0 + bcj : seg_n - 1;
         rbc[S] = ld_off(BCs + static_cast<int64_t>(rr) * N, static_cast<unsigned>(bcn) * sizeof(Tin));
@@ -384,15 +411,19 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
       ed[P] = dsk * xv;
     }
   };
-  auto epilogue = [&](auto pc, int c, float g, float dx) __attribute__((always_inline)) {
+  // STEADY: chunk c is the one before the steady iteration's own (the running offset
+  // under RUN)
+  auto epilogue = [&](auto pc, auto steadyc, int c, float g, float dx) __attribute__((always_inline)) {
     constexpr int P = decltype(pc)::value;
+    constexpr bool STEADY = decltype(steadyc)::value;
     if constexpr (OUT) {
       const int l = c * T + w;
-      if (l < seg_n && dvalid) {
+      const int64_t yoff = (STEADY && RUN) ? run_dim + off_e : static_cast<int64_t>(l) * dim;
+      if ((STEADY || l < seg_n) && dvalid) {
         // the four partials of timestep w (group k = w / 4, j = w % 4) of this channel
         const float* src = &s_yp[P][w >> 2][w & 3][0][lane + 8 * (w >> 2)];
         const float v = (src[0] + src[YR + 2]) + (src[2 * YR + 4] + src[3 * YR + 6]);
-        store_val(at_off(Yb + static_cast<int64_t>(l) * dim, static_cast<unsigned>(lane) * sizeof(Tin)), (v + dx) * g);
+        store_val(at_off(Yb + yoff, static_cast<unsigned>(lane) * sizeof(Tin)), (v + dx) * g);
       }
     }
   };
@@ -456,7 +487,7 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
       if (STEADY || c + 3 < nchunks) gload(Par<Q>{}, steadyc, c + 3);
     }
     if (STEADY || c >= 1) {
-      epilogue(Par<Q>{}, c - 1, pg, pd);
+      epilogue(Par<Q>{}, steadyc, c - 1, pg, pd);
       ckpt_store(Par<Q>{}, c - 1);
     }
     float p[T];
@@ -572,19 +603,25 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
     // steady iterations: c >= 1 and chunks c + 1 .. c + 3 full (pairs, so the LDS
     // buffer and load register set indices stay compile-time constants)
     int c = 1;
+    run_dim = Tdim;
+    run_bc = TN;
     for (; c + 4 < nfull; c += 2) {
       iteration(Par<1>{}, std::true_type{}, c);
+      run_dim += Tdim;
+      run_bc += TN;
       iteration(Par<0>{}, std::true_type{}, c + 1);
+      run_dim += Tdim;
+      run_bc += TN;
     }
     for (; c < nchunks; c += 2) {
       iteration(Par<1>{}, std::false_type{}, c);
       if (c + 1 < nchunks) iteration(Par<0>{}, std::false_type{}, c + 1);
     }
     if ((nchunks - 1) & 1) {
-      epilogue(Par<1>{}, nchunks - 1, eg[1], ed[1]);
+      epilogue(Par<1>{}, std::false_type{}, nchunks - 1, eg[1], ed[1]);
       ckpt_store(Par<1>{}, nchunks - 1);
     } else {
-      epilogue(Par<0>{}, nchunks - 1, eg[0], ed[0]);
+      epilogue(Par<0>{}, std::false_type{}, nchunks - 1, eg[0], ed[0]);
       ckpt_store(Par<0>{}, nchunks - 1);
     }
   }
