@@ -757,17 +757,23 @@ __global__ __launch_bounds__(1024) void bwd_agg_row_kernel(
   // Two register sets of loaded inputs: a chunk's loads are issued two iterations
   // before it is staged, so that their latency is hidden behind two chunks of steps.
   Tin r_dt[2], r_z[2], r_dy[2], r_c[2];
+  // Steady iterations (chunk c >= 4) load chunk c - 3, which is full, through running
+  // offsets advanced by subtraction: run_ld = (c - 3) T dim, run_c = (c - 3) T N.
+  const int64_t Tdim = static_cast<int64_t>(T) * dim, TN = static_cast<int64_t>(T) * N;
+  const int64_t woff = static_cast<int64_t>(w) * dim, coff = static_cast<int64_t>(crow) * N + cn;
+  int64_t run_ld = 0, run_c = 0;
   // loads of chunk c into set S; positions past the segment end read its last row
   // (those steps become identities in the staging)
-  auto gload = [&](auto sc, int c) {
+  auto gload = [&](auto sc, auto steadyc, int c) {
     constexpr int S = decltype(sc)::value;
+    constexpr bool STEADY = decltype(steadyc)::value;
     const int l = c * T + w;
-    const int64_t off = static_cast<int64_t>(l < seg_n ? l : seg_n - 1) * dim;
+    const int64_t off = STEADY ? run_ld + woff : static_cast<int64_t>(l < seg_n ? l : seg_n - 1) * dim;
     r_dt[S] = ld_off(DTb + off, dlane);
     r_dy[S] = ld_off(DYb + off, dlane);
     r_z[S] = ld_off(Zb + off, dlane);
     const int t = c * T + crow;
-    r_c[S] = Cs[static_cast<int64_t>(t < seg_n ? t : seg_n - 1) * N + cn];
+    r_c[S] = Cs[STEADY ? run_c + coff : static_cast<int64_t>(t < seg_n ? t : seg_n - 1) * N + cn];
   };
   // stage chunk c from register set S into LDS buffer P
   auto stage = [&](auto pc, auto sc, int c) {
@@ -802,7 +808,7 @@ __global__ __launch_bounds__(1024) void bwd_agg_row_kernel(
     read_c(3);
     if (STEADY || c > 0) {
       stage(Par<Q>{}, Par<Q>{}, c - 1);
-      if (STEADY || c > 2) gload(Par<Q>{}, c - 3);
+      if (STEADY || c > 2) gload(Par<Q>{}, steadyc, c - 3);
     }
     static_for<0, T>([&](auto ic) {
       constexpr int t = T - 1 - decltype(ic)::value;
@@ -818,17 +824,23 @@ __global__ __launch_bounds__(1024) void bwd_agg_row_kernel(
     __syncthreads();
   };
   if (nch > 0) {
-    gload(Par<0>{}, nch - 1);
+    gload(Par<0>{}, std::false_type{}, nch - 1);
     stage(Par<0>{}, Par<0>{}, nch - 1);
-    if (nch > 1) gload(Par<1>{}, nch - 2);
-    if (nch > 2) gload(Par<0>{}, nch - 3);
+    if (nch > 1) gload(Par<1>{}, std::false_type{}, nch - 2);
+    if (nch > 2) gload(Par<0>{}, std::false_type{}, nch - 3);
     __syncthreads();
     // buffer and register-set parities follow the processing order, so they stay
     // compile-time constants
     int c = nch - 1;
+    run_ld = static_cast<int64_t>(c - 3) * Tdim;
+    run_c = static_cast<int64_t>(c - 3) * TN;
     for (; c >= 4; c -= 2) {
       iteration(Par<0>{}, std::true_type{}, c);
+      run_ld -= Tdim;
+      run_c -= TN;
       iteration(Par<1>{}, std::true_type{}, c - 1);
+      run_ld -= Tdim;
+      run_c -= TN;
     }
     for (; c >= 1; c -= 2) {
       iteration(Par<0>{}, std::false_type{}, c);

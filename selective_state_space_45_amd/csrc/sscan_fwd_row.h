@@ -293,6 +293,9 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
   const int64_t off_e = static_cast<int64_t>(w) * dim - Tdim;
   const int64_t off_bc = 3 * TN + static_cast<int64_t>(bcrow0) * N;
   int64_t run_dim = 0, run_bc = 0;
+  // CKRUN: the steady checkpoint stores from the same running offset (N == T == 16)
+  constexpr bool CKRUN = CKPT && NFIX == 16 && T == 16;
+  const int64_t ck_steady = ((b * sh.nblk + 2 * (l_begin / T) - 2) * N + w) * dim;
   // Two register sets for the global loads, by chunk parity: chunk c's loads are
   // issued two iterations before its prologue consumes them.
   Tin rx[2], rdt[2], rz[2], rbc[2], rdy[2];
@@ -434,14 +437,22 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
     constexpr int P = decltype(pc)::value;
     if constexpr (CKPT) s_ck[P][half][ln][cr] = h;
   };
-  auto ckpt_store = [&](auto pc, int c) __attribute__((always_inline)) {
+  // STEADY (N == 16): chunk c is the one before the steady iteration's own, full, so
+  // both of its blocks exist; block 2 (l_begin / T + c) + half lies at ck_steady +
+  // (2 c + half) N dim, and 2 c N dim = 2 run_dim when N == T.
+  auto ckpt_store = [&](auto pc, auto steadyc, int c) __attribute__((always_inline)) {
     constexpr int P = decltype(pc)::value;
+    constexpr bool STEADY = decltype(steadyc)::value;
     if constexpr (CKPT) {
       if (w < N && dvalid) {
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          const int64_t kb = 2 * (l_begin / T + c) + half;
-          if (kb < sh.nblk) ckpt[((b * sh.nblk + kb) * N + w) * dim + d] = s_ck[P][half][w][lane];
+          if constexpr (STEADY && CKRUN) {
+            ckpt[ck_steady + 2 * run_dim + half * Tdim + d] = s_ck[P][half][w][lane];
+          } else {
+            const int64_t kb = 2 * (l_begin / T + c) + half;
+            if (kb < sh.nblk) ckpt[((b * sh.nblk + kb) * N + w) * dim + d] = s_ck[P][half][w][lane];
+          }
         }
       }
     }
@@ -488,7 +499,7 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
     }
     if (STEADY || c >= 1) {
       epilogue(Par<Q>{}, steadyc, c - 1, pg, pd);
-      ckpt_store(Par<Q>{}, c - 1);
+      ckpt_store(Par<Q>{}, steadyc, c - 1);
     }
     float p[T];
     // AGG: the reverse aggregate's share of step t (see the adjoint note)
@@ -619,10 +630,10 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
     }
     if ((nchunks - 1) & 1) {
       epilogue(Par<1>{}, std::false_type{}, nchunks - 1, eg[1], ed[1]);
-      ckpt_store(Par<1>{}, nchunks - 1);
+      ckpt_store(Par<1>{}, std::false_type{}, nchunks - 1);
     } else {
       epilogue(Par<0>{}, std::false_type{}, nchunks - 1, eg[0], ed[0]);
-      ckpt_store(Par<0>{}, nchunks - 1);
+      ckpt_store(Par<0>{}, std::false_type{}, nchunks - 1);
     }
   }
   if constexpr (OUT) {
