@@ -45,8 +45,9 @@ __global__ __launch_bounds__(256) void carry_kernel(const float* __restrict__ ag
   const float a = A[d * N + n];
   float c = h_init ? h_init[i] : 0.f;
   // Segments in groups of G: the group's aggregates are loaded together, so their
-  // latencies overlap instead of adding up along the sequential combine.
-  constexpr int G = 8;
+  // latencies overlap instead of adding up along the sequential combine (one round
+  // of loads for up to 16 segments).
+  constexpr int G = 16;
   for (int s0 = 0; s0 < nseg; s0 += G) {
     float hv[G], sv[G];
 #pragma unroll
