@@ -402,6 +402,7 @@ struct BwdLayout {
   int64_t seg_len;
   int bseg;                // reverse pass segments
   int64_t seg_blocks;      // kBwdBlock-step blocks per reverse segment
+  bool shared;             // the two passes share their segments (below)
 };
 
 // Reverse-pass segments: two reverse-kernel workgroups are resident per CU (LDS).  A
@@ -417,6 +418,15 @@ int bwd_segments(int64_t batch, int64_t seqlen, int64_t dim) {
   return static_cast<int>(pick_segments_out(base, seqlen, 2 * cus));
 }
 
+// Segments of the two passes.  When the checkpoint pass is itself split (a grid of
+// fewer workgroups than CUs) and N == 16, it takes the reverse pass's segment count
+// and the reverse pass takes its segments: then every checkpoint workgroup also forms
+// its segment's reverse aggregate (the kFwdCkptAgg mode with per-segment aggregates),
+// and the reverse pass skips its aggregate sweep.  Both passes run in rounds of the
+// same length at either count (the checkpoint pass one workgroup per CU with
+// segments of L/S steps, the reverse pass two per CU), so the shared count costs the
+// checkpoint pass nothing measurable, and its forward aggregate pass gains rounds
+// that are better filled (long context: 64 segments instead of 32).
 BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t N) {
   BwdLayout lo{};
   const int64_t nblk = (seqlen + sscan::kBwdBlock - 1) / sscan::kBwdBlock;
@@ -426,6 +436,18 @@ BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t N) {
   if (lo.seg_blocks < 1) lo.seg_blocks = 1;
   lo.bseg = static_cast<int>((nblk + lo.seg_blocks - 1) / lo.seg_blocks);
   if (lo.bseg < 1) lo.bseg = 1;
+  SegPlan pl = plan_segments(batch, seqlen, dim, N, 0, ~size_t(0), true, sscan::kFwdCkpt);
+  lo.shared = false;
+  if (N == 16 && pl.nseg > 1 && lo.bseg > 1) {
+    const SegPlan ps = plan_segments(batch, seqlen, dim, N, lo.bseg, ~size_t(0), true, sscan::kFwdCkpt);
+    const int64_t sb = ps.seg_len / sscan::kBwdBlock;
+    if (ps.nseg > 1 && ps.seg_len % sscan::kChunk == 0 && (nblk + sb - 1) / sb == ps.nseg) {
+      pl = ps;
+      lo.seg_blocks = sb;
+      lo.bseg = ps.nseg;
+      lo.shared = true;
+    }
+  }
   const size_t bdn = static_cast<size_t>(batch) * dim * N;
   size_t off = 0;
   lo.gB = off;   off += round256(static_cast<size_t>(ndt) * batch * N * seqlen * 4);
@@ -433,7 +455,6 @@ BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t N) {
   lo.gA = off;   off += round256(static_cast<size_t>(lo.bseg) * bdn * 4);
   lo.gD = off;   off += round256(static_cast<size_t>(lo.bseg) * batch * dim * 4);
   lo.gb = off;   off += round256(static_cast<size_t>(lo.bseg) * batch * dim * 4);
-  const SegPlan pl = plan_segments(batch, seqlen, dim, N, 0, ~size_t(0), true, sscan::kFwdCkpt);
   lo.nseg = pl.nseg;
   lo.seg_len = pl.seg_len;
   lo.seg = off;  off += round256(seg_workspace_bytes(batch, dim, N, pl.nseg));
@@ -538,6 +559,9 @@ int bwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dty
   // sweep and carry kernel are skipped.
   const int64_t rseg_len = lo.seg_blocks * sscan::kBwdBlock;
   const bool agg_in_ckpt = !saved && lo.nseg == 1 && N == 16 && lo.bseg == 2 && rseg_len % sscan::kChunk == 0;
+  // a split checkpoint pass whose segments the reverse pass shares forms the reverse
+  // aggregates of every segment (bwd_layout)
+  const bool seg_agg = !saved && lo.shared;
   hipError_t e;
   if (!saved) {
   // 1. checkpoints: the forward recurrence, storing the state entering every chunk
@@ -577,6 +601,13 @@ int bwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dty
     p.gin = reinterpret_cast<float*>(ws + lo.gin);
     p.rseg_len = rseg_len;
     e = sscan::launch_fwd_checkpoints_agg(p, bf16, s);
+  } else if (seg_agg) {
+    p.z = z;
+    p.dy = dy;
+    p.gin = reinterpret_cast<float*>(ws + lo.rg);
+    p.ragg_s = reinterpret_cast<float*>(ws + lo.rs);
+    p.rseg_len = 0;
+    e = sscan::launch_fwd_checkpoints_agg(p, bf16, s);
   } else {
     e = sscan::launch_fwd_checkpoints(p, bf16, s);
   }
@@ -604,6 +635,7 @@ int bwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dty
   q.ragg_s = reinterpret_cast<float*>(ws + lo.rs);
   q.gin = reinterpret_cast<float*>(ws + lo.gin);
   q.carry_done = agg_in_ckpt;
+  q.agg_done = seg_agg;
   e = sscan::launch_bwd(q, bf16, s);
   if (e != hipSuccess) return hip_fail(e, "backward launch");
   return ok();

@@ -990,7 +990,9 @@ void launch_bwd_one(const BwdParams& p, hipStream_t s) {
   BwdShape sh{p.batch, p.L, p.dim, p.ndtiles, p.nblk, p.seg_blocks, p.N, p.nseg};
   if (p.nseg > 1 && !p.carry_done) {   // else gin was formed by the checkpoint pass
     const dim3 agrid(static_cast<unsigned>(p.ndtiles * p.batch * (p.nseg - 1)));
-    if constexpr (NF == 16) {
+    if (p.agg_done) {
+      // the aggregates came from the checkpoint pass
+    } else if constexpr (NF == 16) {
       hipLaunchKernelGGL((bwd_agg_row_kernel<Tin>), agrid, dim3(1024), 0, s, static_cast<const Tin*>(p.dt),
                          static_cast<const Tin*>(p.z), static_cast<const Tin*>(p.C), static_cast<const Tin*>(p.dy),
                          p.A, p.bias, p.ragg_g, p.ragg_s, sh);

@@ -127,7 +127,11 @@ __device__ __forceinline__ void row_reduce_partial16(const float (&p)[16], float
 // step, instead of a separate reverse sweep that recomputes Delta and Abar.  The
 // kernel then writes the reverse pass's two segment carries itself.  One forward
 // segment (the sweep starts at position 0); rseg_len is a multiple of kChunk, so the
-// second segment starts at a chunk start and ends with the last chunk.
+// second segment starts at a chunk start and ends with the last chunk.  With
+// rseg_len == 0 every chunk aggregates: the reverse pass's segments are then the
+// forward sweep's own (any number of them, each workgroup starting from its carried
+// state), and each workgroup writes its segment's G and sum of Delta*log2(e) for the
+// reverse pass's carry kernel.
 template <typename Tin, int MODE, int NFIX, bool EULER, bool STRUCT = false>
 __global__ __launch_bounds__(1024) void fwd_row_kernel(
     const Tin* __restrict__ xg, const Tin* __restrict__ dtg, const Tin* __restrict__ zg,
@@ -135,7 +139,7 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
     const float* __restrict__ Dg, const float* __restrict__ biasg, const float* __restrict__ h_init,
     Tin* __restrict__ yg, float* __restrict__ h_last, float* __restrict__ ckpt, const float* __restrict__ conv_w,
     const float* __restrict__ conv_b, const float* __restrict__ conv_s, const Tin* __restrict__ dyg,
-    const float* __restrict__ dlast, float* __restrict__ gin, FwdShape sh) {
+    const float* __restrict__ dlast, float* __restrict__ gin, float* __restrict__ ragg_s, FwdShape sh) {
   constexpr bool CONV = MODE == kFwdOutConv;
   constexpr bool OUT = MODE == kFwdOut || MODE == kFwdOutCkpt || CONV;
   constexpr bool AGG = MODE == kFwdCkptAgg;
@@ -640,19 +644,27 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
     if (h_last && seg == sh.nseg - 1 && drvalid && nlive) h_last[(b * dim + dr) * N + ln] = h;
   }
   if constexpr (AGG) {
-    // The reverse pass's segment carries, formed as its carry kernel forms them: the
-    // gradient entering the end of segment 1 is dLoss/d(last state) (or 0), the one
-    // entering the end of segment 0 is exp2(A S) gl + G, with S the second segment's sum
-    // of Delta*log2(e): the per-wave sums its last prologue staged (the last chunk's
-    // barrier has passed), added in wave order.
+    // S: the aggregated steps' sum of Delta*log2(e), from the per-wave sums the last
+    // prologue staged (the last chunk's barrier has passed), added in wave order.
+    // rseg_len > 0: the reverse pass's two segment carries, formed as its carry kernel
+    // forms them: the gradient entering the end of segment 1 is dLoss/d(last state)
+    // (or 0), the one entering the end of segment 0 is exp2(A S) gl + G.
+    // rseg_len == 0: this segment's reverse aggregate G and S, as the backward pass's
+    // aggregate kernel writes them for the segment (its carry kernel chains them).
     if (nchunks > 0 && agg_chunk(nchunks - 1) && drvalid) {
       float S = 0.f;
 #pragma unroll
       for (int q = 0; q < 16; ++q) S += s_sum[q][cr];
-      const int64_t i = (b * dim + dr) * 16 + ln;
-      const float gl = dlast ? dlast[i] : 0.f;
-      gin[sh.batch * dim * 16 + i] = gl;
-      gin[i] = fmaf(hw_exp2(Av * S), gl, qg);
+      if (sh.rseg_len > 0) {
+        const int64_t i = (b * dim + dr) * 16 + ln;
+        const float gl = dlast ? dlast[i] : 0.f;
+        gin[sh.batch * dim * 16 + i] = gl;
+        gin[i] = fmaf(hw_exp2(Av * S), gl, qg);
+      } else {
+        const int64_t row = static_cast<int64_t>(seg) * sh.batch + b;
+        gin[(row * dim + dr) * 16 + ln] = qg;
+        if (ln == 0) ragg_s[row * dim + dr] = S;
+      }
     }
   }
 }
@@ -663,7 +675,7 @@ void launch_row_one(const FwdParams& p, dim3 grid, hipStream_t s) {
   hipLaunchKernelGGL((fwd_row_kernel<Tin, MODE, NF, EU, ST>), grid, dim3(1024), 0, s, static_cast<const Tin*>(p.x),
                      static_cast<const Tin*>(p.dt), static_cast<const Tin*>(p.z), static_cast<const Tin*>(p.B),
                      static_cast<const Tin*>(p.C), p.A, p.Dskip, p.bias, p.h_init, static_cast<Tin*>(p.y), p.h_last,
-                     p.ckpt, p.conv_w, p.conv_b, p.conv_s, static_cast<const Tin*>(p.dy), p.dlast, p.gin, sh);
+                     p.ckpt, p.conv_w, p.conv_b, p.conv_s, static_cast<const Tin*>(p.dy), p.dlast, p.gin, p.ragg_s, sh);
 }
 
 // Launch of one (mode, discretization rule) variant of the row layout (N <= 16).
@@ -674,9 +686,11 @@ hipError_t launch_fwd_row(const FwdParams& p, bool bf16, hipStream_t s) {
   if (nblocks <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(nblocks));
   if constexpr (MODE == kFwdCkptAgg) {
-    // N == 16, one forward segment, a second reverse segment starting at a chunk start
-    if (p.N != 16 || p.nseg != 1 || p.rseg_len <= 0 || p.rseg_len % kChunk != 0 || p.rseg_len >= p.L)
-      return hipErrorInvalidValue;
+    // N == 16, and either one forward segment and a second reverse segment starting at
+    // a chunk start, or per-segment reverse aggregates (rseg_len == 0)
+    if (p.N != 16 || p.rseg_len < 0 || !p.gin) return hipErrorInvalidValue;
+    if (p.rseg_len > 0 && (p.nseg != 1 || p.rseg_len % kChunk != 0 || p.rseg_len >= p.L)) return hipErrorInvalidValue;
+    if (p.rseg_len == 0 && !p.ragg_s) return hipErrorInvalidValue;
     if (bf16)
       launch_row_one<bf16_t, MODE, 16, EU>(p, grid, s);
     else

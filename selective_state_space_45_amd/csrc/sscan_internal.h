@@ -40,12 +40,18 @@ struct FwdParams {
   const float* conv_b;    // nullable: [dim]
   const float* conv_s;    // nullable: raw inputs before the sequence [batch][dim][dconv-1]
   int dconv;
-  // kFwdCkptAgg: the output gradient and dLoss/d(last state) (nullable), and the
-  // backward pass's gin [2][batch][dim][N] (as its carry kernel forms it) for two
-  // reverse segments, the second starting at rseg_len (a multiple of kChunk below L)
+  // kFwdCkptAgg: the output gradient and dLoss/d(last state) (nullable), and either
+  //  - rseg_len > 0: the backward pass's gin [2][batch][dim][N] (as its carry kernel
+  //    forms it) for two reverse segments, the second starting at rseg_len (a multiple
+  //    of kChunk below L), one forward segment; or
+  //  - rseg_len == 0: the reverse aggregate of each forward segment, which is also a
+  //    reverse segment, into gin as [nseg][batch][dim][N] and its sum of
+  //    Delta*log2(e) into ragg_s [nseg][batch][dim] (what the backward pass's
+  //    aggregate kernel writes; its carry kernel then chains them).
   const void* dy;
   const float* dlast;
   float* gin;
+  float* ragg_s;
   int64_t rseg_len;
   int64_t batch, L, dim;
   int64_t seg_len;        // timesteps per segment (multiple of kChunk unless nseg == 1)
@@ -122,6 +128,8 @@ struct BwdParams {
   int nseg;
   bool euler;
   bool carry_done;        // gin already written (by the kFwdCkptAgg checkpoint pass)
+  bool agg_done;          // ragg_g / ragg_s already written (by the kFwdCkptAgg checkpoint
+                          // pass with per-segment aggregates); the carry kernel still runs
 };
 
 struct BwdShape {

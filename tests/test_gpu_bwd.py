@@ -106,6 +106,29 @@ def test_bwd_aggregates_in_checkpoint_pass_small_A_no_gate(ss, orc):
     check_bwd(ss, orc, w, with_dlast=False)
 
 
+# A split checkpoint pass whose segments the reverse pass shares (N = 16, fewer
+# workgroups than CUs): every checkpoint workgroup also forms its segment's reverse
+# aggregate and the separate aggregate sweep is skipped.  (2, 1000, 200): 8 workgroups
+# per segment (a ragged channel tile), 13 segments of 80 steps for both passes, the
+# last one 40 steps (a ragged chunk); an initial state, dLoss/d(last state), and
+# channels whose waves take the small-|A| forms (A = 0 included).
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("euler", [False, True])
+def test_bwd_shared_segments(ss, orc, dtype, euler):
+    w = W.make_scan_inputs(2, 1000, 200, 16, dtype, seed=512, name="bwd shared segments")
+    w.A = w.A.copy()
+    w.A[64:68, :] = -1e-3
+    w.A[130, 2] = 0.0
+    h0 = np.random.default_rng(12).standard_normal((2, 200, 16)).astype(np.float32)
+    check_bwd(ss, orc, w, h0=h0, euler=euler)
+
+
+def test_bwd_shared_segments_no_gate(ss, orc):
+    # the same path with no z (gy = dy) and no final-state gradient
+    w = W.make_scan_inputs(2, 1000, 200, 16, "f32", seed=513, with_z=False, name="bwd shared segments, no gate")
+    check_bwd(ss, orc, w, with_dlast=False)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_bwd_optional_inputs_absent(ss, orc, dtype):
     w = W.make_scan_inputs(1, 70, 64, 16, dtype, seed=502, with_z=False, with_D=False, with_bias=False,
