@@ -278,8 +278,8 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
 #pragma unroll
   for (int k = 0; k < KC; ++k) tapoff[k] = ((K - 1 - k) < 0 ? 0 : (K - 1 - k)) * dim;
 
-  // AGG: chunk c holds aggregate work when it lies in the second reverse segment
-  // (workgroup-uniform); the last chunk hands over the sums
+  // AGG: chunk c holds aggregate work when it lies in the second reverse segment, or
+  // always when rseg_len == 0 (workgroup-uniform); the last chunk hands over the sums
   auto agg_chunk = [&](int c) __attribute__((always_inline)) { return AGG && c * T >= sh.rseg_len; };
   float qg = 0.f, pr = 1.f;          // G and the running product of Abar (lane = state)
   float ssum = 0.f, scomp = 0.f;     // Kahan sum of the staged Delta*log2(e) (lane = channel)
