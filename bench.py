@@ -16,9 +16,13 @@ region's average launch (HIP events around the K steps; one launch per step), wh
 is what a kernel trace of the same run averages; roofline.flushed holds the median.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
-                    [--no-euler] [--no-structured] [--no-bwd] [--no-conv] [--copy-calibration]
+                    [--no-euler] [--no-structured] [--no-bwd] [--no-conv] [--no-copy-ref]
+                    [--copy-calibration]
     python bench.py --summarize-counters FETCH_CSV WRITE_CSV   (CPU only)
     python bench.py --configs     (one line per workload: GPU time, GB/s, oracle time, error)
+
+copy_reference times a plain 512 MiB -> 512 MiB elementwise copy like the other legs;
+roofline.frac_of_copy and decode.frac_of_copy put the achieved rates against it.
 
 --copy-calibration also runs a plain 512 MiB -> 512 MiB elementwise copy (three
 times), the known-size reference that scales the HBM byte counters read by
@@ -329,6 +333,7 @@ def main():
     ap.add_argument("--no-structured", action="store_true", help="skip the structured-A leg")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward-pass leg")
     ap.add_argument("--no-conv", action="store_true", help="skip the convolution-prologue leg")
+    ap.add_argument("--no-copy-ref", action="store_true", help="skip the reference copy leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 512 MiB elementwise copy (counter calibration)")
     ap.add_argument("--kernel-runs", type=int, default=60,
@@ -534,6 +539,24 @@ def main():
                             f"replayed {reps} times"}
         del states, g
 
+    # Reference: a plain elementwise copy (512 MiB of fp32 read, 512 MiB written), timed
+    # as the other legs: the bandwidth this machine's HBM gives a kernel that only streams.
+    # The forward's and the decode step's achieved rates are also reported against it.
+    copy_ref = None
+    if not args.no_copy_ref:
+        src = torch.ones(COPY_ELEMS, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        cp_ms = leg_ms(lambda: torch.mul(src, 1.0, out=dst), nruns)
+        cp_gbs = 2 * COPY_ELEMS * 4 / (cp_ms * 1e-3) / 1e9
+        copy_ref = {"op": "torch.mul(src, 1.0, out=dst): 512 MiB fp32 read, 512 MiB written",
+                    "ms": round(cp_ms, 5), "gbs": round(cp_gbs, 2),
+                    "hbm_frac_of_peak": round(cp_gbs / PEAK_HBM_GBS, 4),
+                    "timing": f"median of {nruns} launches, HIP events, each after the cache flush"}
+        roof["frac_of_copy"] = round(roof["achieved"] / cp_gbs, 4)
+        if decode is not None:
+            decode["frac_of_copy"] = round(decode["gbs"] / cp_gbs, 4)
+        del src, dst
+
     if args.copy_calibration:
         src = torch.ones(COPY_ELEMS, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -597,6 +620,7 @@ def main():
         "conv": conv,
         "bwd": bwd,
         "decode": decode,
+        "copy_reference": copy_ref,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
