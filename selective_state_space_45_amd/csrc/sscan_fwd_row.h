@@ -113,6 +113,9 @@ __device__ __forceinline__ void row_reduce_partial16(const float (&p)[16], float
 // the prologue stages x / c_d with Delta and B / a_n with B (both shared work), and each
 // step forms k with one multiply instead of two.  The workgroup verifies the form on its
 // tile exactly and takes the plain staging where it does not hold.
+// ZK (output modes): the gate z as a compile-time fact, 1 present and 2 absent (no z
+// loads, y without the SiLU factor; zero-order hold only), or 0 read from zg at run
+// time.  Fixing it spares the per-chunk select between SiLU(z) and 1.
 //
 // Adjoint note (kFwdCkptAgg).  The backward pass runs the adjoint recurrence
 // g_{t-1} = Abar_t (g_t + C_t gy_t) from the sequence end (gy = dy silu(z): the
@@ -132,7 +135,7 @@ __device__ __forceinline__ void row_reduce_partial16(const float (&p)[16], float
 // forward sweep's own (any number of them, each workgroup starting from its carried
 // state), and each workgroup writes its segment's G and sum of Delta*log2(e) for the
 // reverse pass's carry kernel.
-template <typename Tin, int MODE, int NFIX, bool EULER, bool STRUCT = false>
+template <typename Tin, int MODE, int NFIX, bool EULER, bool STRUCT = false, int ZK = 0>
 __global__ __launch_bounds__(1024) void fwd_row_kernel(
     const Tin* __restrict__ xg, const Tin* __restrict__ dtg, const Tin* __restrict__ zg,
     const Tin* __restrict__ Bg, const Tin* __restrict__ Cg, const float* __restrict__ Ag,
@@ -151,6 +154,8 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
   static_assert(T == 16, "one staged timestep per lane of a row");
   static_assert(!CKPT || 2 * kBwdBlock == T, "checkpoints are taken at half chunks");
   static_assert(!STRUCT || (MODE == kFwdOut && !EULER), "the factored staging serves the plain ZOH output mode");
+  static_assert(ZK == 0 || OUT, "z fixed at compile time in the output modes only");
+  static_assert(ZK != 2 || !EULER, "the Euler rule reads an absent gate at run time");
   // LDS layouts.  Row strides are chosen so that each read below touches distinct
   // banks (16 lanes for 64-bit accesses, 32 for 32-bit ones, 8 for 128-bit ones).
   // (Delta*log2(e), x) [timestep][channel] (Delta*x for the Euler rule): the
@@ -212,7 +217,7 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
   const int64_t tok0 = (b * L + l_begin) * dim + dtile * kTile;
   const Tin* __restrict__ Xb = xg + tok0;
   const Tin* __restrict__ DTb = dtg + tok0;
-  const bool hasZ = (OUT || AGG) && zg != nullptr;
+  const bool hasZ = ZK == 1 || (ZK == 0 && (OUT || AGG) && zg != nullptr);
   const Tin* __restrict__ Zb = hasZ ? zg + tok0 : xg + tok0;
   Tin* __restrict__ Yb = OUT ? yg + tok0 : nullptr;
   const Tin* __restrict__ DYb = AGG ? dyg + tok0 : xg + tok0;
@@ -337,7 +342,7 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
       rx[S] = ld_off(Xb + off, dlane);
     }
     rdt[S] = ld_off(DTb + off, dlane);
-    if constexpr (OUT) rz[S] = ld_off(Zb + off, dlane);
+    if constexpr (OUT && ZK != 2) rz[S] = ld_off(Zb + off, dlane);
     const bool ag = agg_chunk(c);
     if constexpr (AGG) {
       if (ag) {
@@ -418,6 +423,18 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
       ed[P] = dsk * xv;
     }
   };
+  // Read bases (in floats from s_yp) of the epilogue's four partials: the pair at
+  // partials 0 and 1 and the pair at 2 and 3, for each parity.  The second parity's
+  // buffer lies beyond the reach of ds_read2's 8-bit offsets; the empty asm hides how
+  // its bases derive from the first parity's, so that they stay in registers instead of
+  // being formed again with two adds every chunk.
+  const int yp_a0 = ((w >> 2) * 4 + (w & 3)) * 4 * YR + lane + 8 * (w >> 2);
+  const int yp_b0 = yp_a0 + 2 * YR + 4;
+  int yp_a1 = yp_a0 + 4 * 4 * 4 * YR, yp_b1 = yp_b0 + 4 * 4 * 4 * YR;
+  if constexpr (OUT) {
+    asm volatile("" : "+v"(yp_a1));
+    asm volatile("" : "+v"(yp_b1));
+  }
   // STEADY: chunk c is the one before the steady iteration's own (the running offset
   // under RUN)
   auto epilogue = [&](auto pc, auto steadyc, int c, float g, float dx) __attribute__((always_inline)) {
@@ -428,8 +445,9 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
       const int64_t yoff = (STEADY && RUN) ? run_dim + off_e : static_cast<int64_t>(l) * dim;
       if ((STEADY || l < seg_n) && dvalid) {
         // the four partials of timestep w (group k = w / 4, j = w % 4) of this channel
-        const float* src = &s_yp[P][w >> 2][w & 3][0][lane + 8 * (w >> 2)];
-        const float v = (src[0] + src[YR + 2]) + (src[2 * YR + 4] + src[3 * YR + 6]);
+        const float* sa = &s_yp[0][0][0][0][0] + (P ? yp_a1 : yp_a0);
+        const float* sb = &s_yp[0][0][0][0][0] + (P ? yp_b1 : yp_b0);
+        const float v = (sa[0] + sa[YR + 2]) + (sb[0] + sb[YR + 2]);
         store_val(at_off(Yb + yoff, static_cast<unsigned>(lane) * sizeof(Tin)), (v + dx) * g);
       }
     }
@@ -669,13 +687,32 @@ __global__ __launch_bounds__(1024) void fwd_row_kernel(
   }
 }
 
-template <typename Tin, int MODE, int NF, bool EU, bool ST = false>
+template <typename Tin, int MODE, int NF, bool EU, bool ST = false, int ZK = 0>
 void launch_row_one(const FwdParams& p, dim3 grid, hipStream_t s) {
   FwdShape sh{p.batch, p.L, p.dim, p.seg_len, p.ndtiles, p.nblk, p.rseg_len, p.N, p.nseg, p.dconv};
-  hipLaunchKernelGGL((fwd_row_kernel<Tin, MODE, NF, EU, ST>), grid, dim3(1024), 0, s, static_cast<const Tin*>(p.x),
+  hipLaunchKernelGGL((fwd_row_kernel<Tin, MODE, NF, EU, ST, ZK>), grid, dim3(1024), 0, s, static_cast<const Tin*>(p.x),
                      static_cast<const Tin*>(p.dt), static_cast<const Tin*>(p.z), static_cast<const Tin*>(p.B),
                      static_cast<const Tin*>(p.C), p.A, p.Dskip, p.bias, p.h_init, static_cast<Tin*>(p.y), p.h_last,
                      p.ckpt, p.conv_w, p.conv_b, p.conv_s, static_cast<const Tin*>(p.dy), p.dlast, p.gin, p.ragg_s, sh);
+}
+
+// N == 16 output modes: the variant with the gate's presence fixed (ZK of
+// fwd_row_kernel); the others read it at run time.  The Euler rule's gate-absent
+// variant is left out: the compiler placed its recurrence's row broadcasts inside an
+// exec-masked block, where a DPP read from a switched-off lane gives zero; it keeps
+// the run-time test, whose code has none there.
+template <typename Tin, int MODE, bool EU, bool ST>
+void launch_row_n16(const FwdParams& p, dim3 grid, hipStream_t s) {
+  if constexpr (MODE == kFwdOut || MODE == kFwdOutCkpt || MODE == kFwdOutConv) {
+    if (p.z)
+      launch_row_one<Tin, MODE, 16, EU, ST, 1>(p, grid, s);
+    else if constexpr (!EU)
+      launch_row_one<Tin, MODE, 16, EU, ST, 2>(p, grid, s);
+    else
+      launch_row_one<Tin, MODE, 16, EU, ST>(p, grid, s);
+  } else {
+    launch_row_one<Tin, MODE, 16, EU, ST>(p, grid, s);
+  }
 }
 
 // Launch of one (mode, discretization rule) variant of the row layout (N <= 16).
@@ -698,12 +735,12 @@ hipError_t launch_fwd_row(const FwdParams& p, bool bf16, hipStream_t s) {
   } else {
     if (bf16) {
       if (p.N == 16)
-        launch_row_one<bf16_t, MODE, 16, EU, ST>(p, grid, s);
+        launch_row_n16<bf16_t, MODE, EU, ST>(p, grid, s);
       else
         launch_row_one<bf16_t, MODE, 0, EU, ST>(p, grid, s);
     } else {
       if (p.N == 16)
-        launch_row_one<float, MODE, 16, EU, ST>(p, grid, s);
+        launch_row_n16<float, MODE, EU, ST>(p, grid, s);
       else
         launch_row_one<float, MODE, 0, EU, ST>(p, grid, s);
     }

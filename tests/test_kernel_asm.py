@@ -99,11 +99,16 @@ def test_checker_flags_a_masked_dpp():
 
 
 @pytest.mark.skipif(_hipcc() is None, reason="hipcc not found")
-def test_row_kernel_dpp_runs_with_full_rows(tmp_path):
-    asm = _compile_asm("sscan_fwd_row_zoh.hip", str(tmp_path / "row_zoh.s"))
+@pytest.mark.parametrize("src,count", [("sscan_fwd_row_zoh.hip", 16), ("sscan_fwd_row_euler.hip", 16),
+                                       ("sscan_fwd_row_struct.hip", 6)])
+def test_row_kernel_dpp_runs_with_full_rows(tmp_path, src, count):
+    asm = _compile_asm(src, str(tmp_path / src.replace(".hip", ".s")))
     res = dpp_under_partial_exec(asm, r"_ZN5sscan14fwd_row_kernel\w+")
-    # output, checkpoint and output+checkpoint modes, bf16 and fp32, N = 16 and any N
-    assert len(res) == 12, sorted(res)
+    # zero-order hold and Euler: output, checkpoint and output+checkpoint modes, bf16
+    # and fp32, N = 16 and any N, the N = 16 output modes once with the gate present
+    # and once without (Euler: with the gate read at run time); structured A: the
+    # output mode alone
+    assert len(res) == count, sorted(res)
     for name, (total, masked) in res.items():
         assert total >= 16, (name, total)     # at least the 16 row broadcasts of a chunk
         assert masked == 0, "%s: %d DPP instructions inside an exec-masked block" % (name, masked)
@@ -131,7 +136,8 @@ def test_row_kernel_conv_dpp_runs_with_full_rows(tmp_path):
     # before the sequence start must not take the recurrence's broadcasts with it
     asm = _compile_asm("sscan_fwd_row_conv.hip", str(tmp_path / "row_conv.s"))
     res = dpp_under_partial_exec(asm, r"_ZN5sscan14fwd_row_kernel\w+")
-    assert len(res) == 8, sorted(res)   # both rules, bf16 and fp32, N = 16 and any N
+    # both rules, bf16 and fp32, N = 16 (gate present and absent) and any N
+    assert len(res) == 12, sorted(res)
     for name, (total, masked) in res.items():
         assert total >= 16, (name, total)
         assert masked == 0, "%s: %d DPP instructions inside an exec-masked block" % (name, masked)
