@@ -136,7 +136,8 @@ def test_row_kernel_conv_dpp_runs_with_full_rows(tmp_path):
     # before the sequence start must not take the recurrence's broadcasts with it
     asm = _compile_asm("sscan_fwd_row_conv.hip", str(tmp_path / "row_conv.s"))
     res = dpp_under_partial_exec(asm, r"_ZN5sscan14fwd_row_kernel\w+")
-    # both rules, bf16 and fp32, N = 16 (gate present and absent) and any N
+    # both rules, bf16 and fp32, any N and N = 16 twice (the gate present, and absent
+    # or, under the Euler rule, read at run time)
     assert len(res) == 12, sorted(res)
     for name, (total, masked) in res.items():
         assert total >= 16, (name, total)
